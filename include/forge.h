@@ -1,0 +1,186 @@
+/*
+ * forge.h -- C ABI of the fused weight-gradient + optimizer-step library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the FORGE explainer pages (gist.science, "FORGE:
+ * Fused On-Register Gradient Elimination for Memory-Efficient LLM Training").
+ *   - Technical Summary section 1 "The Problem": the standard schedule writes
+ *     the full weight gradient of a layer to HBM and the optimizer reads it
+ *     back.
+ *   - Technical Summary section 2 "Core Mechanism": for each 128 x 128 tile of
+ *     W the kernel accumulates the products of the upstream gradient dY and the
+ *     input X over all tokens in fp32 registers, applies the optimizer to the
+ *     tile in registers, discards the gradient, and writes back only the
+ *     updated weight tile and its moment tiles.
+ *   - Technical Summary section 2 "Precision and Fidelity": the gradient stays
+ *     fp32; the bf16 weight write-back is rounded stochastically; int8
+ *     optimizer states use blocks of 64 elements.
+ *   - Technical Summary section 3 "Key Contributions": eight element-wise
+ *     optimizers (AdamW, NAdam, RAdam, Lion, RMSprop, AdaGrad, SGD,
+ *     SGD-momentum).
+ *   - Technical Summary section 4 "Composability": fp8 inputs.
+ *   - Technical Summary section 5 "Significance and Claims" (limitations): the
+ *     input gradient must be read before the weight update; weights with
+ *     several gradient consumers in one step are excluded.
+ *
+ * Conventions for every entry point
+ *   - Tensors are row-major and contiguous; every data pointer is a device
+ *     pointer to memory of the current HIP device, aligned to 16 bytes.  All
+ *     buffers are owned by the caller; the library keeps no pointer after a
+ *     call returns and holds no mutable global state.
+ *   - Shapes: X[T, K] layer input, dY[T, N] upstream gradient, W[N, K] weight
+ *     (PyTorch nn.Linear layout), dW[N, K], dX[T, K].  N and K must be
+ *     multiples of 128; T may be any value >= 0 (a ragged final token slab is
+ *     handled; T = 0 means a zero gradient).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; arguments are validated synchronously first.  On any
+ *     error nothing is launched and no buffer is touched.
+ *   - No entry point allocates device memory.
+ *   - Thread safety: entry points may be called from several threads; the
+ *     text of the last error is kept per thread.
+ */
+#ifndef FORGE_H
+#define FORGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FORGE_VERSION 100 /* 1.0.0 */
+
+typedef enum forge_status {
+  FORGE_OK = 0,
+  FORGE_ERR_ARG = 1,    /* null pointer, step < 1, unknown enum, state given/missing for the rule */
+  FORGE_ERR_SHAPE = 2,  /* shapes disagree, N or K not a multiple of 128, N*K >= 2^32 */
+  FORGE_ERR_DTYPE = 3,  /* unsupported dtype or dtype combination */
+  FORGE_ERR_LAYOUT = 4, /* pointer not 16-byte aligned */
+  FORGE_ERR_ALIAS = 5,  /* an output buffer overlaps an input or another output */
+  FORGE_ERR_DEVICE = 6, /* no device, or the current device is not gfx950 */
+  FORGE_ERR_LAUNCH = 7  /* the HIP runtime refused the launch; see forge_last_error() */
+} forge_status;
+
+typedef enum forge_dtype {
+  FORGE_F32 = 0,
+  FORGE_BF16 = 1,
+  FORGE_FP8_E4M3 = 2, /* OCP e4m3 bytes; `scale` -> one fp32 per-tensor scale (value = decode(code) * scale) */
+  FORGE_I8_B64 = 3,   /* signed int8 moment, codes -127..127; `scale` -> rows*cols/64 fp32 block absmax */
+  FORGE_U8_B64 = 4    /* non-negative uint8 moment, codes 0..255; `scale` -> rows*cols/64 fp32 block absmax */
+} forge_dtype;
+
+typedef enum forge_opt {
+  FORGE_ADAMW = 0,        /* states m, v */
+  FORGE_NADAM = 1,        /* states m, v */
+  FORGE_RADAM = 2,        /* states m, v */
+  FORGE_LION = 3,         /* state m */
+  FORGE_RMSPROP = 4,      /* state v */
+  FORGE_ADAGRAD = 5,      /* state v (sum of squared gradients) */
+  FORGE_SGD = 6,          /* no state */
+  FORGE_SGD_MOMENTUM = 7  /* state m (momentum buffer) */
+} forge_opt;
+
+/* A 2-D tensor descriptor.  `scale` is a device pointer (see forge_dtype) or NULL. */
+typedef struct forge_tensor {
+  void* data;
+  int32_t dtype; /* forge_dtype */
+  int64_t rows;
+  int64_t cols;
+  void* scale;
+} forge_tensor;
+
+/* Weight-decay modes. DEFAULT: decoupled for AdamW and Lion, coupled L2 for the others. */
+#define FORGE_WD_DEFAULT 0
+#define FORGE_WD_DECOUPLED 1
+#define FORGE_WD_L2 2
+
+/* Hyper-parameters.  Fields a rule does not use are ignored.
+ *   AdamW/NAdam/RAdam: lr, beta1, beta2, eps, weight_decay; NAdam also momentum_decay (psi).
+ *   Lion: lr, beta1 (interpolation inside sign), beta2 (moment), weight_decay.
+ *   RMSprop: lr, alpha, eps, weight_decay.   AdaGrad: lr, eps, weight_decay.
+ *   SGD: lr, weight_decay.   SGD-momentum: lr, momentum, weight_decay. */
+typedef struct forge_hyper {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t wd_mode;
+  float momentum, alpha, momentum_decay;
+} forge_hyper;
+
+/* Optional per-call options (pass NULL for the defaults). */
+typedef struct forge_step_opts {
+  float* w_preround_out; /* if non-NULL: fp32 [N, K] device buffer receiving the updated weight
+                            before it is rounded to the storage dtype (for checking) */
+  int32_t sr_enable;     /* bf16 weights: 1 = stochastic rounding (default), 0 = nearest-even */
+} forge_step_opts;
+
+/*
+ * forge_wgrad_step -- one fused optimizer step of a linear layer's weight.
+ *
+ * For every element of W: g = sum_t dY[t, n] * X[t, k] accumulated in fp32 (for fp8 inputs
+ * multiplied by both per-tensor scales), then one step of rule `opt` updates W, m, v in place.
+ * The gradient is never written to memory (Technical Summary section 2 "Core Mechanism").
+ *
+ *   X, dY   inputs, both F32, both BF16 or both FP8_E4M3.  Read only.
+ *   W       [N, K], F32 (fp32 inputs only) or BF16.  BF16 is written back with stochastic
+ *           rounding: element i = n*K + k draws 16 bits from Philox4x64-10 with counter
+ *           (i >> 4, step, 0, 0) and key (seed, 0), field (i & 3) of word (i & 15) >> 2, and
+ *           stores (bits(fp32 value) + r) >> 16 (NaN stays NaN).
+ *   m, v    moments of the rule ([N, K], F32, or I8_B64 for m / U8_B64 for v with their block
+ *           scales); must be NULL for a moment the rule does not keep.  Zero them before step 1.
+ *   step    1-based step count used by bias corrections and schedules; must be >= 1.
+ *   seed    stochastic-rounding key; give each weight its own seed.
+ * Errors: see forge_status.  A weight with several gradient consumers in one step (tied
+ * embeddings, shared experts) or a non-element-wise update (global-norm clipping) cannot use
+ * this call (Technical Summary section 5, limitations).
+ */
+forge_status forge_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                              forge_tensor* m, forge_tensor* v, const forge_hyper* hyper,
+                              int32_t opt, int64_t step, uint64_t seed,
+                              const forge_step_opts* opts, void* stream);
+
+/*
+ * forge_dgrad -- input gradient dX[T, K] = dY[T, N] . W[N, K] (fp32 accumulation, stored BF16
+ * with round-to-nearest-even, or F32).  dY and W BF16 (or both F32).  It reads W as it is when
+ * the kernel runs, so enqueue it before forge_wgrad_step on the same stream (Technical Summary
+ * section 5: the input gradient must be read before the weight update).
+ */
+forge_status forge_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX,
+                         void* stream);
+
+/* forge_linear_backward_step -- forge_dgrad then forge_wgrad_step, in that order, on `stream`. */
+forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tensor* dY,
+                                        forge_tensor* W, forge_tensor* dX, forge_tensor* m,
+                                        forge_tensor* v, const forge_hyper* hyper, int32_t opt,
+                                        int64_t step, uint64_t seed, const forge_step_opts* opts,
+                                        void* stream);
+
+/*
+ * Unfused two-phase baseline (Technical Summary section 1 "The Problem"): the gradient is
+ * materialised in a caller-owned fp32 buffer dW[N, K] and a separate kernel applies the rule.
+ * The contraction and the rule are the same device code as the fused path, so for the same
+ * inputs forge_wgrad_gemm + forge_optimizer_step give bitwise the results of forge_wgrad_step.
+ */
+forge_status forge_wgrad_gemm(const forge_tensor* X, const forge_tensor* dY, forge_tensor* dW,
+                              void* stream);
+forge_status forge_optimizer_step(const forge_tensor* dW, forge_tensor* W, forge_tensor* m,
+                                  forge_tensor* v, const forge_hyper* hyper, int32_t opt,
+                                  int64_t step, uint64_t seed, const forge_step_opts* opts,
+                                  void* stream);
+
+/*
+ * forge_step_scalars -- host only, no GPU needed: the per-step scalars (computed in fp64,
+ * rounded to fp32) that the kernels receive for rule `opt` at step `step`.  Writes up to
+ * n_out floats: {decay, l2, c1, c2, c3, b1, omb1, b2, omb2, eps, lr, rectified}.
+ */
+forge_status forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, float* out,
+                                int32_t n_out);
+
+const char* forge_status_string(forge_status s);
+const char* forge_last_error(void); /* text of this thread's last error ("" if none) */
+int32_t forge_version(void);
+/* FORGE_OK if `device` exists and is a gfx950 part. */
+forge_status forge_device_check(int32_t device);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FORGE_H */

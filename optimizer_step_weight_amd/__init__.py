@@ -1,0 +1,210 @@
+"""Python binding of libforge.so, the fused weight-gradient + optimizer step for MI355X.
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels.  Tensors are PyTorch device tensors (PyTorch provides device memory and the
+stream); they are passed to the C ABI as raw pointers and sizes.  If the library is not
+built, every call raises: there is no fallback path.
+
+Entry points (same names as the C ABI in include/forge.h, without the ``forge_`` prefix):
+    wgrad_step, dgrad, linear_backward_step, wgrad_gemm, optimizer_step,
+    step_scalars, device_check, version, status_string, last_error
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libforge.so")
+
+OPT = {"adamw": 0, "nadam": 1, "radam": 2, "lion": 3, "rmsprop": 4, "adagrad": 5, "sgd": 6, "sgd_momentum": 7}
+F32, BF16, FP8_E4M3, I8_B64, U8_B64 = 0, 1, 2, 3, 4
+STATUS = {0: "FORGE_OK", 1: "FORGE_ERR_ARG", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_DTYPE", 4: "FORGE_ERR_LAYOUT",
+          5: "FORGE_ERR_ALIAS", 6: "FORGE_ERR_DEVICE", 7: "FORGE_ERR_LAUNCH"}
+SCALARS = ("decay", "l2", "c1", "c2", "c3", "b1", "omb1", "b2", "omb2", "eps", "lr", "rectified")
+
+
+class ForgeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("scale", ctypes.c_void_p)]
+
+
+class Hyper(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("wd_mode", ctypes.c_int32),
+                ("momentum", ctypes.c_float), ("alpha", ctypes.c_float), ("momentum_decay", ctypes.c_float)]
+
+
+class StepOpts(ctypes.Structure):
+    _fields_ = [("w_preround_out", ctypes.c_void_p), ("sr_enable", ctypes.c_int32)]
+
+
+_P = ctypes.POINTER
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(or python -m optimizer_step_weight_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        T, H, O = _P(Tensor), _P(Hyper), _P(StepOpts)
+        st, i32, i64, u64, vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+        L.forge_wgrad_step.argtypes = [T, T, T, T, T, H, i32, i64, u64, O, vp]
+        L.forge_dgrad.argtypes = [T, T, T, vp]
+        L.forge_linear_backward_step.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp]
+        L.forge_wgrad_gemm.argtypes = [T, T, T, vp]
+        L.forge_optimizer_step.argtypes = [T, T, T, T, H, i32, i64, u64, O, vp]
+        L.forge_step_scalars.argtypes = [i32, H, i64, _P(ctypes.c_float), i32]
+        L.forge_status_string.argtypes = [st]
+        L.forge_status_string.restype = ctypes.c_char_p
+        L.forge_last_error.restype = ctypes.c_char_p
+        L.forge_version.restype = i32
+        L.forge_device_check.argtypes = [i32]
+        for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_wgrad_gemm",
+                  "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
+            getattr(L, f).restype = st
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(status: int):
+    if status != 0:
+        raise ForgeError(status, _lib().forge_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    if t.dtype == torch.int8:
+        return I8_B64
+    if t.dtype == torch.uint8:
+        return U8_B64
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t, scale=None) -> Optional[Tensor]:
+    if t is None:
+        return None
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError("tensors must be 2-D and contiguous")
+    return Tensor(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1],
+                  None if scale is None else scale.data_ptr())
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def _hyper(h: Any) -> Hyper:
+    get = (lambda k, d: h.get(k, d)) if isinstance(h, dict) else (lambda k, d: getattr(h, k, d))
+    return Hyper(get("lr", 1e-3), get("beta1", 0.9), get("beta2", 0.999), get("eps", 1e-8),
+                 get("weight_decay", 0.0), int(get("wd_mode", 0)), get("momentum", 0.9), get("alpha", 0.99),
+                 get("momentum_decay", 0.004))
+
+
+def _opt(opt) -> int:
+    return OPT[opt] if isinstance(opt, str) else int(opt)
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _opts(w_preround_out, sr):
+    if w_preround_out is None and sr:
+        return None
+    return StepOpts(None if w_preround_out is None else w_preround_out.data_ptr(), 1 if sr else 0)
+
+
+def wgrad_step(X, dY, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
+               x_scale=None, dy_scale=None, m_scale=None, v_scale=None, w_preround_out=None, sr=True,
+               stream=None):
+    """Fused step: W, m, v updated in place from g = dY^T X (forge_wgrad_step)."""
+    o = _opts(w_preround_out, sr)
+    _check(_lib().forge_wgrad_step(_ref(_tensor(X, x_scale)), _ref(_tensor(dY, dy_scale)), _ref(_tensor(W)),
+                                   _ref(_tensor(m, m_scale)), _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)),
+                                   _opt(opt), int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+
+
+def dgrad(dY, W, dX, *, stream=None):
+    """dX = dY W with the weight as it is now (forge_dgrad)."""
+    _check(_lib().forge_dgrad(_ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _stream(stream)))
+
+
+def linear_backward_step(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
+                         m_scale=None, v_scale=None, w_preround_out=None, sr=True, stream=None):
+    """dgrad then the fused step, in that order (forge_linear_backward_step)."""
+    o = _opts(w_preround_out, sr)
+    _check(_lib().forge_linear_backward_step(
+        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale)),
+        _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+
+
+def wgrad_gemm(X, dY, dW, *, x_scale=None, dy_scale=None, stream=None):
+    """Unfused phase 1: dW = dY^T X written to the fp32 buffer dW (forge_wgrad_gemm)."""
+    _check(_lib().forge_wgrad_gemm(_ref(_tensor(X, x_scale)), _ref(_tensor(dY, dy_scale)), _ref(_tensor(dW)),
+                                   _stream(stream)))
+
+
+def optimizer_step(dW, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int, m_scale=None,
+                   v_scale=None, w_preround_out=None, sr=True, stream=None):
+    """Unfused phase 2: the rule applied to a materialised gradient (forge_optimizer_step)."""
+    o = _opts(w_preround_out, sr)
+    _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale)),
+                                       _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+                                       int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+
+
+def step_scalars(opt, hyper, step: int) -> dict:
+    """Per-step scalars the kernels receive (host only)."""
+    out = (ctypes.c_float * len(SCALARS))()
+    _check(_lib().forge_step_scalars(_opt(opt), ctypes.byref(_hyper(hyper)), int(step), out, len(SCALARS)))
+    return dict(zip(SCALARS, list(out)))
+
+
+def device_check(device: int = 0) -> None:
+    _check(_lib().forge_device_check(int(device)))
+
+
+def version() -> int:
+    return int(_lib().forge_version())
+
+
+def status_string(status: int) -> str:
+    return _lib().forge_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return _lib().forge_last_error().decode()
+
+
+# the C ABI names
+forge_wgrad_step = wgrad_step
+forge_dgrad = dgrad
+forge_linear_backward_step = linear_backward_step
+forge_wgrad_gemm = wgrad_gemm
+forge_optimizer_step = optimizer_step
+forge_step_scalars = step_scalars
+forge_device_check = device_check
+forge_version = version
+forge_status_string = status_string
+forge_last_error = last_error

@@ -1,0 +1,333 @@
+// forge_device.h -- device helpers shared by the fused and the unfused kernels:
+// the element-wise update rules, stochastic rounding of the weight to bf16,
+// the block-64 int8 moment codec, and Philox4x64-10.
+//
+// FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism"
+// (the optimizer runs on the gradient tile held in registers) and "Precision and
+// Fidelity" (fp32 gradient, stochastic rounding of the bf16 weight write-back,
+// int8 states in blocks of 64); section 3 "Key Contributions" (the eight rules).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "forge_internal.h"
+
+namespace forge {
+
+// ------------------------------------------------------------------ Philox4x64-10
+// Salmon et al., "Parallel random numbers: as easy as 1, 2, 3" (SC'11): ten rounds
+// on a 256-bit counter; each round forms the 128-bit products of words 0 and 2 with
+// two odd constants and mixes the halves with words 1, 3 and the key; the key moves
+// by two Weyl constants between rounds.
+struct U64x4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                               uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t lo0 = kM0 * c0, hi0 = __umul64hi(kM0, c0);
+    const uint64_t lo1 = kM1 * c2, hi1 = __umul64hi(kM1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  U64x4 o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+
+// 16 random bits for element j (0..15) of the 16-element block whose Philox output is `o`:
+// field (j & 3) of word j >> 2.
+__device__ __forceinline__ uint32_t sr_field(const U64x4& o, int j) {
+  return (uint32_t)(o.w[j >> 2] >> (16 * (j & 3))) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------ bf16 conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Stochastic rounding: (bits + r) >> 16 rounds the magnitude up with probability
+// (bits mod 2^16) / 2^16; a NaN keeps its sign and becomes quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_sr(float x, uint32_t r16) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t q = (u + r16) >> 16;
+  return (x != x) ? ((u >> 16) | 0x40u) : q;
+}
+
+// Round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t q = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (x != x) ? ((u >> 16) | 0x40u) : q;
+}
+
+// ------------------------------------------------------------------ update rules (fp32)
+// One step of rule OPT for one element.  g: full gradient, w: weight before the step,
+// m / v: moments before the step (updated in place), returns the new fp32 weight.
+// The per-step scalars come from the host (fp64 there, rounded to fp32):
+//   decay = 1 - lr*wd for decoupled decay (else 1); l2 = wd for coupled L2 (else 0).
+template <int OPT>
+__device__ __forceinline__ float rule(float g, float w, float& m, float& v, const OptScalars& s) {
+  g = __builtin_fmaf(s.l2, w, g);
+  const float wd = w * s.decay;
+  if constexpr (OPT == FORGE_OPT_ADAMW) {
+    // c1 = lr / (1 - beta1^t), c2 = 1 / (1 - beta2^t)
+    m = __builtin_fmaf(s.b1, m, s.omb1 * g);
+    v = __builtin_fmaf(s.b2, v, s.omb2 * (g * g));
+    const float den = __builtin_amdgcn_sqrtf(v * s.c2) + s.eps;
+    return __builtin_fmaf(-s.c1, m * __builtin_amdgcn_rcpf(den), wd);
+  } else if constexpr (OPT == FORGE_OPT_NADAM) {
+    // c1 = lr (1 - mu_t) / (1 - prod_t), c2 = 1 / (1 - beta2^t), c3 = lr mu_{t+1} / (1 - prod_{t+1})
+    m = __builtin_fmaf(s.b1, m, s.omb1 * g);
+    v = __builtin_fmaf(s.b2, v, s.omb2 * (g * g));
+    const float den = __builtin_amdgcn_sqrtf(v * s.c2) + s.eps;
+    const float num = __builtin_fmaf(s.c1, g, s.c3 * m);
+    return wd - num * __builtin_amdgcn_rcpf(den);
+  } else if constexpr (OPT == FORGE_OPT_RADAM) {
+    // rectified: c1 = lr r_t sqrt(1 - beta2^t) / (1 - beta1^t); otherwise c1 = lr / (1 - beta1^t)
+    m = __builtin_fmaf(s.b1, m, s.omb1 * g);
+    v = __builtin_fmaf(s.b2, v, s.omb2 * (g * g));
+    if (s.rect) {
+      const float den = __builtin_amdgcn_sqrtf(v) + s.eps;
+      return __builtin_fmaf(-s.c1, m * __builtin_amdgcn_rcpf(den), wd);
+    }
+    return __builtin_fmaf(-s.c1, m, wd);
+  } else if constexpr (OPT == FORGE_OPT_LION) {
+    const float c = __builtin_fmaf(s.b1, m, s.omb1 * g);
+    const float sg = c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
+    m = __builtin_fmaf(s.b2, m, s.omb2 * g);
+    return __builtin_fmaf(-s.lr, sg, wd);
+  } else if constexpr (OPT == FORGE_OPT_RMSPROP) {
+    // b2 = alpha, omb2 = 1 - alpha
+    v = __builtin_fmaf(s.b2, v, s.omb2 * (g * g));
+    const float den = __builtin_amdgcn_sqrtf(v) + s.eps;
+    return __builtin_fmaf(-s.lr, g * __builtin_amdgcn_rcpf(den), wd);
+  } else if constexpr (OPT == FORGE_OPT_ADAGRAD) {
+    v = __builtin_fmaf(g, g, v);
+    const float den = __builtin_amdgcn_sqrtf(v) + s.eps;
+    return __builtin_fmaf(-s.lr, g * __builtin_amdgcn_rcpf(den), wd);
+  } else if constexpr (OPT == FORGE_OPT_SGD) {
+    return __builtin_fmaf(-s.lr, g, wd);
+  } else {  // SGD with momentum: c1 = momentum
+    m = __builtin_fmaf(s.c1, m, g);
+    return __builtin_fmaf(-s.lr, m, wd);
+  }
+}
+
+template <int OPT>
+struct RuleStates {
+  static constexpr bool m = OPT == FORGE_OPT_ADAMW || OPT == FORGE_OPT_NADAM || OPT == FORGE_OPT_RADAM ||
+                            OPT == FORGE_OPT_LION || OPT == FORGE_OPT_SGD_MOMENTUM;
+  static constexpr bool v = OPT == FORGE_OPT_ADAMW || OPT == FORGE_OPT_NADAM || OPT == FORGE_OPT_RADAM ||
+                            OPT == FORGE_OPT_RMSPROP || OPT == FORGE_OPT_ADAGRAD;
+};
+
+// ------------------------------------------------------------------ vector memory helpers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
+
+// ------------------------------------------------------------------ one 16-element segment
+// Applies rule OPT to 16 consecutive elements of one row of W, starting at flat index i0
+// (a multiple of 16).  The weight, moments and scales are read and written here.  For int8
+// moments the 64-element block spans the 4 consecutive lanes lane^1, lane^2 (all four must
+// be active); the lane holding the block's first segment writes the block scale.
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void step_segment16(const float (&g)[16], uint32_t i0, const EpiArgs& e) {
+  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
+  float w[16], m[16], v[16];
+
+  // --- loads
+  if constexpr (WT == FORGE_W_BF16) {
+    const uint16_t* wp = static_cast<const uint16_t*>(e.W) + i0;
+    u32x4 a = ld16(wp), b = ld16(wp + 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[2 * q] = __uint_as_float(a[q] << 16);
+      w[2 * q + 1] = __uint_as_float(a[q] & 0xFFFF0000u);
+      w[8 + 2 * q] = __uint_as_float(b[q] << 16);
+      w[8 + 2 * q + 1] = __uint_as_float(b[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float* wp = static_cast<const float*>(e.W) + i0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 a = ld16(wp + 4 * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[4 * q + c] = __uint_as_float(a[c]);
+    }
+  }
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
+      const float* mp = static_cast<const float*>(e.m) + i0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 a = ld16(mp + 4 * q);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = __uint_as_float(a[c]);
+      }
+    } else {
+      const u32x4 a = ld16(static_cast<const int8_t*>(e.m) + i0);
+      const float f = e.m_scale[i0 >> 6] * (1.0f / 127.0f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = (float)(int8_t)(a[q] >> (8 * c)) * f;
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+      const float* vp = static_cast<const float*>(e.v) + i0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 a = ld16(vp + 4 * q);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = __uint_as_float(a[c]);
+      }
+    } else {
+      const u32x4 a = ld16(static_cast<const uint8_t*>(e.v) + i0);
+      const float f = e.v_scale[i0 >> 6] * (1.0f / 255.0f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = (float)((a[q] >> (8 * c)) & 0xFFu) * f;
+    }
+  }
+
+  // --- the rule, element by element
+  float wn[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float mj = HM ? m[j] : 0.0f, vj = HV ? v[j] : 0.0f;
+    wn[j] = rule<OPT>(g[j], w[j], mj, vj, e.s);
+    m[j] = mj;
+    v[j] = vj;
+  }
+
+  if (e.w_pre) {
+    float* pp = e.w_pre + i0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 a;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(wn[4 * q + c]);
+      st16(pp + 4 * q, a);
+    }
+  }
+
+  // --- weight write-back
+  if constexpr (WT == FORGE_W_BF16) {
+    uint32_t r[16];
+    if (e.sr) {
+      const U64x4 o = philox4x64_10((uint64_t)(i0 >> 4), e.step, 0ull, 0ull, e.seed, 0ull);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) r[j] = f32_to_bf16_sr(wn[j], sr_field(o, j));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) r[j] = f32_to_bf16_rne(wn[j]);
+    }
+    u32x4 a, b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = r[2 * q] | (r[2 * q + 1] << 16);
+      b[q] = r[8 + 2 * q] | (r[8 + 2 * q + 1] << 16);
+    }
+    uint16_t* wp = static_cast<uint16_t*>(e.W) + i0;
+    st16(wp, a);
+    st16(wp + 8, b);
+  } else {
+    float* wp = static_cast<float*>(e.W) + i0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 a;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(wn[4 * q + c]);
+      st16(wp + 4 * q, a);
+    }
+  }
+
+  // --- moment write-back
+  const bool leader = ((i0 >> 4) & 3u) == 0u;
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
+      float* mp = static_cast<float*>(e.m) + i0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(m[4 * q + c]);
+        st16(mp + 4 * q, a);
+      }
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(m[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      u32x4 a;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float qv = __builtin_rintf(m[4 * q + c] * inv);
+          qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+          word |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * c);
+        }
+        a[q] = word;
+      }
+      st16(static_cast<int8_t*>(e.m) + i0, a);
+      if (leader) e.m_scale[i0 >> 6] = amax;
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+      float* vp = static_cast<float*>(e.v) + i0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[4 * q + c]);
+        st16(vp + 4 * q, a);
+      }
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const float inv = amax > 0.0f ? 255.0f / amax : 0.0f;
+      u32x4 a;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float qv = __builtin_rintf(v[4 * q + c] * inv);
+          qv = fminf(fmaxf(qv, 0.0f), 255.0f);
+          word |= ((uint32_t)qv & 0xFFu) << (8 * c);
+        }
+        a[q] = word;
+      }
+      st16(static_cast<uint8_t*>(e.v) + i0, a);
+      if (leader) e.v_scale[i0 >> 6] = amax;
+    }
+  }
+}
+
+}  // namespace forge

@@ -1,0 +1,431 @@
+// forge_host.cpp -- the C ABI declared in include/forge.h: argument validation, per-step
+// scalars (fp64 on the host, handed to the kernels as fp32), device check and dispatch.
+//
+// Validation runs before any HIP call, so a bad call returns its error code without a GPU
+// being touched (and without one being present).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "forge.h"
+#include "forge_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+forge_status fail(forge_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+int64_t dtype_size(int32_t dt) {
+  switch (dt) {
+    case FORGE_F32: return 4;
+    case FORGE_BF16: return 2;
+    case FORGE_FP8_E4M3:
+    case FORGE_I8_B64:
+    case FORGE_U8_B64: return 1;
+  }
+  return 0;
+}
+
+bool rule_has_m(int32_t opt) {
+  return opt == FORGE_ADAMW || opt == FORGE_NADAM || opt == FORGE_RADAM || opt == FORGE_LION ||
+         opt == FORGE_SGD_MOMENTUM;
+}
+bool rule_has_v(int32_t opt) {
+  return opt == FORGE_ADAMW || opt == FORGE_NADAM || opt == FORGE_RADAM || opt == FORGE_RMSPROP ||
+         opt == FORGE_ADAGRAD;
+}
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  const char* name = "";
+};
+
+Range range_of(const void* p, int64_t bytes, const char* name) {
+  Range r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + (uintptr_t)(bytes > 0 ? bytes : 0);
+  r.name = name;
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+forge_status check_tensor(const forge_tensor* t, const char* name) {
+  if (!t) return fail(FORGE_ERR_ARG, "%s is NULL", name);
+  if (t->rows < 0 || t->cols < 0) return fail(FORGE_ERR_SHAPE, "%s has a negative dimension", name);
+  if (dtype_size(t->dtype) == 0) return fail(FORGE_ERR_DTYPE, "%s has unknown dtype %d", name, (int)t->dtype);
+  if (t->rows * t->cols > 0 && !t->data) return fail(FORGE_ERR_ARG, "%s->data is NULL", name);
+  if (!aligned16(t->data)) return fail(FORGE_ERR_LAYOUT, "%s->data is not 16-byte aligned", name);
+  return FORGE_OK;
+}
+
+int64_t bytes_of(const forge_tensor* t) { return t->rows * t->cols * dtype_size(t->dtype); }
+
+// device check, cached per device
+std::atomic<int> g_dev_ok[64];
+
+forge_status device_ok() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FORGE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64 && g_dev_ok[dev].load(std::memory_order_relaxed) == 1) return FORGE_OK;
+  return forge_device_check(dev);
+}
+
+forge_status to_status(int herr) {
+  if (herr == (int)hipSuccess) return FORGE_OK;
+  return fail(FORGE_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)herr));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ per-step scalars
+static forge_status compute_scalars(int32_t opt, const forge_hyper* h, int64_t step, forge::OptScalars* out) {
+  if (!h) return fail(FORGE_ERR_ARG, "hyper is NULL");
+  if (opt < FORGE_ADAMW || opt > FORGE_SGD_MOMENTUM) return fail(FORGE_ERR_ARG, "unknown optimizer %d", (int)opt);
+  if (step < 1) return fail(FORGE_ERR_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  if (h->wd_mode < FORGE_WD_DEFAULT || h->wd_mode > FORGE_WD_L2)
+    return fail(FORGE_ERR_ARG, "unknown wd_mode %d", (int)h->wd_mode);
+  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, eps = h->eps, wd = h->weight_decay;
+  const double t = (double)step;
+  const bool dec = h->wd_mode == FORGE_WD_DECOUPLED ||
+                   (h->wd_mode == FORGE_WD_DEFAULT && (opt == FORGE_ADAMW || opt == FORGE_LION));
+  forge::OptScalars s{};
+  s.decay = (float)(dec ? 1.0 - lr * wd : 1.0);
+  s.l2 = (float)(dec ? 0.0 : wd);
+  s.b1 = (float)b1;
+  s.omb1 = (float)(1.0 - b1);
+  s.b2 = (float)b2;
+  s.omb2 = (float)(1.0 - b2);
+  s.eps = (float)eps;
+  s.lr = (float)lr;
+  s.rect = 0;
+  const double bc1 = 1.0 - std::pow(b1, t), bc2 = 1.0 - std::pow(b2, t);
+  switch (opt) {
+    case FORGE_ADAMW:
+      s.c1 = (float)(lr / bc1);
+      s.c2 = (float)(1.0 / bc2);
+      break;
+    case FORGE_NADAM: {
+      // momentum schedule mu_i = beta1 (1 - 0.5 * 0.96^(i psi)); prod_t = mu_1 ... mu_t
+      const double psi = h->momentum_decay;
+      double prod = 1.0;
+      for (int64_t i = 1; i <= step; ++i) prod *= b1 * (1.0 - 0.5 * std::pow(0.96, (double)i * psi));
+      const double mu = b1 * (1.0 - 0.5 * std::pow(0.96, t * psi));
+      const double mu_next = b1 * (1.0 - 0.5 * std::pow(0.96, (t + 1.0) * psi));
+      s.c1 = (float)(lr * (1.0 - mu) / (1.0 - prod));
+      s.c2 = (float)(1.0 / bc2);
+      s.c3 = (float)(lr * mu_next / (1.0 - prod * mu_next));
+      break;
+    }
+    case FORGE_RADAM: {
+      const double rho_inf = 2.0 / (1.0 - b2) - 1.0;
+      const double rho_t = rho_inf - 2.0 * t * std::pow(b2, t) / bc2;
+      if (rho_t > 5.0) {
+        const double r = std::sqrt((rho_t - 4.0) * (rho_t - 2.0) * rho_inf / ((rho_inf - 4.0) * (rho_inf - 2.0) * rho_t));
+        s.rect = 1;
+        s.c1 = (float)(lr * r * std::sqrt(bc2) / bc1);
+      } else {
+        s.c1 = (float)(lr / bc1);
+      }
+      break;
+    }
+    case FORGE_RMSPROP:
+      s.b2 = (float)(double)h->alpha;
+      s.omb2 = (float)(1.0 - (double)h->alpha);
+      break;
+    case FORGE_SGD_MOMENTUM:
+      s.c1 = (float)(double)h->momentum;
+      break;
+    default:
+      break;
+  }
+  *out = s;
+  return FORGE_OK;
+}
+
+// ------------------------------------------------------------------ shared validation of the step
+struct StepPlan {
+  int w_type = 0, s_type = 0;
+  forge::EpiArgs e{};
+};
+
+static forge_status validate_step_outputs(int64_t N, int64_t K, forge_tensor* W, forge_tensor* m, forge_tensor* v,
+                                          const forge_hyper* hyper, int32_t opt, int64_t step, uint64_t seed,
+                                          const forge_step_opts* opts, StepPlan* plan, Range* outs, int* n_outs) {
+  forge_status st;
+  if ((st = check_tensor(W, "W")) != FORGE_OK) return st;
+  if (W->rows != N || W->cols != K)
+    return fail(FORGE_ERR_SHAPE, "W is [%lld, %lld], expected [%lld, %lld]", (long long)W->rows, (long long)W->cols,
+                (long long)N, (long long)K);
+  if (N % 128 || K % 128)
+    return fail(FORGE_ERR_SHAPE, "N = %lld and K = %lld must be multiples of 128", (long long)N, (long long)K);
+  if (N * K >= (int64_t(1) << 32)) return fail(FORGE_ERR_SHAPE, "N * K must be below 2^32");
+  if (W->dtype != FORGE_F32 && W->dtype != FORGE_BF16) return fail(FORGE_ERR_DTYPE, "W must be F32 or BF16");
+
+  forge::OptScalars s;
+  if ((st = compute_scalars(opt, hyper, step, &s)) != FORGE_OK) return st;
+
+  const bool need_m = rule_has_m(opt), need_v = rule_has_v(opt);
+  if (need_m != (m != nullptr))
+    return fail(FORGE_ERR_ARG, need_m ? "this rule keeps a first moment m: pass it" : "this rule keeps no m: pass NULL");
+  if (need_v != (v != nullptr))
+    return fail(FORGE_ERR_ARG, need_v ? "this rule keeps a second moment v: pass it" : "this rule keeps no v: pass NULL");
+  int s_type = -1;
+  int n = 0;
+  outs[n++] = range_of(W->data, bytes_of(W), "W");
+  for (int which = 0; which < 2; ++which) {
+    forge_tensor* t = which ? v : m;
+    const char* name = which ? "v" : "m";
+    if (!t) continue;
+    if ((st = check_tensor(t, name)) != FORGE_OK) return st;
+    if (t->rows != N || t->cols != K) return fail(FORGE_ERR_SHAPE, "%s must have the shape of W", name);
+    int ty;
+    if (t->dtype == FORGE_F32) ty = forge::FORGE_S_F32;
+    else if (t->dtype == (which ? FORGE_U8_B64 : FORGE_I8_B64)) ty = forge::FORGE_S_Q8;
+    else return fail(FORGE_ERR_DTYPE, "%s must be F32 or %s", name, which ? "U8_B64" : "I8_B64");
+    if (s_type >= 0 && ty != s_type) return fail(FORGE_ERR_DTYPE, "m and v must both be fp32 or both be 8-bit");
+    s_type = ty;
+    outs[n++] = range_of(t->data, bytes_of(t), name);
+    if (ty == forge::FORGE_S_Q8) {
+      if (!t->scale) return fail(FORGE_ERR_ARG, "%s->scale (block scales) is NULL", name);
+      if (!aligned4(t->scale)) return fail(FORGE_ERR_LAYOUT, "%s->scale is not 4-byte aligned", name);
+      outs[n++] = range_of(t->scale, N * K / 64 * 4, which ? "v scales" : "m scales");
+    }
+  }
+  if (s_type < 0) s_type = forge::FORGE_S_F32;
+  float* w_pre = opts ? opts->w_preround_out : nullptr;
+  if (w_pre) {
+    if (!aligned16(w_pre)) return fail(FORGE_ERR_LAYOUT, "w_preround_out is not 16-byte aligned");
+    outs[n++] = range_of(w_pre, N * K * 4, "w_preround_out");
+  }
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlap(outs[i], outs[j])) return fail(FORGE_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  *n_outs = n;
+
+  plan->w_type = W->dtype == FORGE_BF16 ? forge::FORGE_W_BF16 : forge::FORGE_W_F32;
+  plan->s_type = s_type;
+  forge::EpiArgs& e = plan->e;
+  e.W = W->data;
+  e.m = m ? m->data : nullptr;
+  e.v = v ? v->data : nullptr;
+  e.m_scale = m ? static_cast<float*>(m->scale) : nullptr;
+  e.v_scale = v ? static_cast<float*>(v->scale) : nullptr;
+  e.w_pre = w_pre;
+  e.seed = seed;
+  e.step = (uint64_t)step;
+  e.sr = opts ? (opts->sr_enable != 0) : 1;
+  e.s = s;
+  return FORGE_OK;
+}
+
+static forge_status validate_inputs(const forge_tensor* X, const forge_tensor* dY, int* in_type, forge::GemmArgs* g,
+                                    Range* ins, int* n_ins) {
+  forge_status st;
+  if ((st = check_tensor(X, "X")) != FORGE_OK) return st;
+  if ((st = check_tensor(dY, "dY")) != FORGE_OK) return st;
+  if (X->dtype != dY->dtype) return fail(FORGE_ERR_DTYPE, "X and dY must have the same dtype");
+  if (X->dtype == FORGE_F32) *in_type = forge::FORGE_IN_F32;
+  else if (X->dtype == FORGE_BF16) *in_type = forge::FORGE_IN_BF16;
+  else if (X->dtype == FORGE_FP8_E4M3) *in_type = forge::FORGE_IN_FP8;
+  else return fail(FORGE_ERR_DTYPE, "X and dY must be F32, BF16 or FP8_E4M3");
+  if (X->rows != dY->rows)
+    return fail(FORGE_ERR_SHAPE, "X has %lld tokens, dY has %lld", (long long)X->rows, (long long)dY->rows);
+  int n = 0;
+  ins[n++] = range_of(X->data, bytes_of(X), "X");
+  ins[n++] = range_of(dY->data, bytes_of(dY), "dY");
+  g->x_scale = g->dy_scale = nullptr;
+  if (*in_type == forge::FORGE_IN_FP8) {
+    if (!X->scale || !dY->scale) return fail(FORGE_ERR_ARG, "fp8 inputs need their per-tensor scale pointers");
+    if (!aligned4(X->scale) || !aligned4(dY->scale)) return fail(FORGE_ERR_LAYOUT, "fp8 scale not 4-byte aligned");
+    g->x_scale = static_cast<const float*>(X->scale);
+    g->dy_scale = static_cast<const float*>(dY->scale);
+    ins[n++] = range_of(X->scale, 4, "X scale");
+    ins[n++] = range_of(dY->scale, 4, "dY scale");
+  }
+  g->X = X->data;
+  g->dY = dY->data;
+  g->T = X->rows;
+  g->K = X->cols;
+  g->N = dY->cols;
+  *n_ins = n;
+  return FORGE_OK;
+}
+
+extern "C" {
+
+forge_status forge_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m,
+                              forge_tensor* v, const forge_hyper* hyper, int32_t opt, int64_t step, uint64_t seed,
+                              const forge_step_opts* opts, void* stream) {
+  g_last_error.clear();
+  Range ins[4], outs[6];
+  int n_in = 0, n_out = 0, in_type = 0;
+  forge::GemmArgs g{};
+  forge_status st;
+  if ((st = validate_inputs(X, dY, &in_type, &g, ins, &n_in)) != FORGE_OK) return st;
+  StepPlan plan;
+  if ((st = validate_step_outputs(g.N, g.K, W, m, v, hyper, opt, step, seed, opts, &plan, outs, &n_out)) != FORGE_OK)
+    return st;
+  for (int i = 0; i < n_out; ++i)
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return fail(FORGE_ERR_ALIAS, "%s overlaps %s", outs[i].name, ins[j].name);
+  if (g.N == 0 || g.K == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  return to_status(forge::launch_fused_step(in_type, plan.w_type, plan.s_type, opt, g, plan.e, stream));
+}
+
+forge_status forge_wgrad_gemm(const forge_tensor* X, const forge_tensor* dY, forge_tensor* dW, void* stream) {
+  g_last_error.clear();
+  Range ins[4];
+  int n_in = 0, in_type = 0;
+  forge::GemmArgs g{};
+  forge_status st;
+  if ((st = validate_inputs(X, dY, &in_type, &g, ins, &n_in)) != FORGE_OK) return st;
+  if ((st = check_tensor(dW, "dW")) != FORGE_OK) return st;
+  if (dW->dtype != FORGE_F32) return fail(FORGE_ERR_DTYPE, "dW must be F32");
+  if (dW->rows != g.N || dW->cols != g.K) return fail(FORGE_ERR_SHAPE, "dW must be [N, K]");
+  if (g.N % 128 || g.K % 128) return fail(FORGE_ERR_SHAPE, "N and K must be multiples of 128");
+  if (g.N * g.K >= (int64_t(1) << 32)) return fail(FORGE_ERR_SHAPE, "N * K must be below 2^32");
+  const Range o = range_of(dW->data, bytes_of(dW), "dW");
+  for (int j = 0; j < n_in; ++j)
+    if (overlap(o, ins[j])) return fail(FORGE_ERR_ALIAS, "dW overlaps %s", ins[j].name);
+  if (g.N == 0 || g.K == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  return to_status(forge::launch_wgrad_gemm(in_type, g, static_cast<float*>(dW->data), stream));
+}
+
+forge_status forge_optimizer_step(const forge_tensor* dW, forge_tensor* W, forge_tensor* m, forge_tensor* v,
+                                  const forge_hyper* hyper, int32_t opt, int64_t step, uint64_t seed,
+                                  const forge_step_opts* opts, void* stream) {
+  g_last_error.clear();
+  forge_status st;
+  if ((st = check_tensor(dW, "dW")) != FORGE_OK) return st;
+  if (dW->dtype != FORGE_F32) return fail(FORGE_ERR_DTYPE, "dW must be F32");
+  Range outs[6];
+  int n_out = 0;
+  StepPlan plan;
+  if ((st = validate_step_outputs(dW->rows, dW->cols, W, m, v, hyper, opt, step, seed, opts, &plan, outs, &n_out)) !=
+      FORGE_OK)
+    return st;
+  const Range in = range_of(dW->data, bytes_of(dW), "dW");
+  for (int i = 0; i < n_out; ++i)
+    if (overlap(outs[i], in)) return fail(FORGE_ERR_ALIAS, "%s overlaps dW", outs[i].name);
+  const int64_t n = dW->rows * dW->cols;
+  if (n == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  return to_status(forge::launch_optimizer(plan.w_type, plan.s_type, opt, static_cast<const float*>(dW->data), n,
+                                           plan.e, stream));
+}
+
+forge_status forge_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX, void* stream) {
+  g_last_error.clear();
+  forge_status st;
+  if ((st = check_tensor(dY, "dY")) != FORGE_OK) return st;
+  if ((st = check_tensor(W, "W")) != FORGE_OK) return st;
+  if ((st = check_tensor(dX, "dX")) != FORGE_OK) return st;
+  if (dY->dtype != FORGE_BF16 || W->dtype != FORGE_BF16 || dX->dtype != FORGE_BF16)
+    return fail(FORGE_ERR_DTYPE, "dgrad takes BF16 dY and W and writes BF16 dX");
+  const int64_t T = dY->rows, N = dY->cols, K = W->cols;
+  if (W->rows != N) return fail(FORGE_ERR_SHAPE, "W has %lld rows, dY has %lld columns", (long long)W->rows, (long long)N);
+  if (dX->rows != T || dX->cols != K) return fail(FORGE_ERR_SHAPE, "dX must be [T, K]");
+  if (N % 128 || K % 128) return fail(FORGE_ERR_SHAPE, "N and K must be multiples of 128");
+  const Range o = range_of(dX->data, bytes_of(dX), "dX");
+  if (overlap(o, range_of(dY->data, bytes_of(dY), "dY")) || overlap(o, range_of(W->data, bytes_of(W), "W")))
+    return fail(FORGE_ERR_ALIAS, "dX overlaps an input");
+  if (T == 0 || K == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  return to_status(forge::launch_dgrad(dY->data, W->data, dX->data, T, N, K, stream));
+}
+
+forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                        forge_tensor* dX, forge_tensor* m, forge_tensor* v, const forge_hyper* hyper,
+                                        int32_t opt, int64_t step, uint64_t seed, const forge_step_opts* opts,
+                                        void* stream) {
+  g_last_error.clear();
+  // Validate both calls before enqueueing either, so that an error leaves every buffer untouched.
+  Range ins[4], outs[6];
+  int n_in = 0, n_out = 0, in_type = 0;
+  forge::GemmArgs g{};
+  forge_status st;
+  if ((st = validate_inputs(X, dY, &in_type, &g, ins, &n_in)) != FORGE_OK) return st;
+  StepPlan plan;
+  if ((st = validate_step_outputs(g.N, g.K, W, m, v, hyper, opt, step, seed, opts, &plan, outs, &n_out)) != FORGE_OK)
+    return st;
+  if ((st = check_tensor(dX, "dX")) != FORGE_OK) return st;
+  if (in_type != forge::FORGE_IN_BF16 || W->dtype != FORGE_BF16 || dX->dtype != FORGE_BF16)
+    return fail(FORGE_ERR_DTYPE, "the backward step takes BF16 X, dY, W and dX");
+  if (dX->rows != g.T || dX->cols != g.K) return fail(FORGE_ERR_SHAPE, "dX must be [T, K]");
+  const Range rdx = range_of(dX->data, bytes_of(dX), "dX");
+  for (int i = 0; i < n_out; ++i) {
+    if (overlap(outs[i], rdx)) return fail(FORGE_ERR_ALIAS, "%s overlaps dX", outs[i].name);
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return fail(FORGE_ERR_ALIAS, "%s overlaps %s", outs[i].name, ins[j].name);
+  }
+  for (int j = 0; j < n_in; ++j)
+    if (overlap(rdx, ins[j])) return fail(FORGE_ERR_ALIAS, "dX overlaps %s", ins[j].name);
+  if ((st = forge_dgrad(dY, W, dX, stream)) != FORGE_OK) return st;
+  return forge_wgrad_step(X, dY, W, m, v, hyper, opt, step, seed, opts, stream);
+}
+
+forge_status forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, float* out, int32_t n_out) {
+  g_last_error.clear();
+  forge::OptScalars s;
+  forge_status st = compute_scalars(opt, hyper, step, &s);
+  if (st != FORGE_OK) return st;
+  if (!out && n_out > 0) return fail(FORGE_ERR_ARG, "out is NULL");
+  const float v[12] = {s.decay, s.l2, s.c1, s.c2, s.c3, s.b1, s.omb1, s.b2, s.omb2, s.eps, s.lr, (float)s.rect};
+  for (int i = 0; i < n_out && i < 12; ++i) out[i] = v[i];
+  return FORGE_OK;
+}
+
+const char* forge_status_string(forge_status s) {
+  switch (s) {
+    case FORGE_OK: return "ok";
+    case FORGE_ERR_ARG: return "invalid argument";
+    case FORGE_ERR_SHAPE: return "invalid shape";
+    case FORGE_ERR_DTYPE: return "unsupported dtype";
+    case FORGE_ERR_LAYOUT: return "invalid layout or alignment";
+    case FORGE_ERR_ALIAS: return "overlapping buffers";
+    case FORGE_ERR_DEVICE: return "unsupported device";
+    case FORGE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* forge_last_error(void) { return g_last_error.c_str(); }
+
+int32_t forge_version(void) { return FORGE_VERSION; }
+
+forge_status forge_device_check(int32_t device) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count == 0) return fail(FORGE_ERR_DEVICE, "no HIP device");
+  if (device < 0 || device >= count) return fail(FORGE_ERR_DEVICE, "device %d does not exist", (int)device);
+  hipDeviceProp_t p;
+  e = hipGetDeviceProperties(&p, device);
+  if (e != hipSuccess) return fail(FORGE_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0)
+    return fail(FORGE_ERR_DEVICE, "device %d is %s; this library is built for gfx950", (int)device, p.gcnArchName);
+  if (device < 64) g_dev_ok[device].store(1, std::memory_order_relaxed);
+  return FORGE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// forge_internal.h -- structures shared by the host entry points and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace forge {
+
+enum : int {
+  FORGE_OPT_ADAMW = 0,
+  FORGE_OPT_NADAM = 1,
+  FORGE_OPT_RADAM = 2,
+  FORGE_OPT_LION = 3,
+  FORGE_OPT_RMSPROP = 4,
+  FORGE_OPT_ADAGRAD = 5,
+  FORGE_OPT_SGD = 6,
+  FORGE_OPT_SGD_MOMENTUM = 7,
+};
+
+// input element type of X and dY
+enum : int { FORGE_IN_F32 = 0, FORGE_IN_BF16 = 1, FORGE_IN_FP8 = 2 };
+// weight storage
+enum : int { FORGE_W_F32 = 0, FORGE_W_BF16 = 1 };
+// moment storage
+enum : int { FORGE_S_F32 = 0, FORGE_S_Q8 = 1 };
+
+// Per-step scalars of a rule, computed on the host in fp64 and rounded to fp32.
+struct OptScalars {
+  float decay;  // 1 - lr*wd when weight decay is decoupled, else 1
+  float l2;     // wd when weight decay is coupled (added to the gradient), else 0
+  float c1, c2, c3;
+  float b1, omb1, b2, omb2;
+  float eps, lr;
+  int32_t rect;  // RAdam: rectified branch this step
+};
+
+// Everything the optimizer epilogue needs.
+struct EpiArgs {
+  void* W;         // [N, K] fp32 or bf16
+  void* m;         // [N, K] fp32 or int8 codes, or null
+  void* v;         // [N, K] fp32 or uint8 codes, or null
+  float* m_scale;  // [N*K/64] block absmax (int8 moments)
+  float* v_scale;
+  float* w_pre;    // optional fp32 copy of the weight before rounding
+  uint64_t seed;
+  uint64_t step;
+  int32_t sr;      // bf16 weight: stochastic (1) or nearest-even (0) rounding
+  OptScalars s;
+};
+
+// The contraction dW = dY^T X.
+struct GemmArgs {
+  const void* X;   // [T, K]
+  const void* dY;  // [T, N]
+  const float* x_scale;   // fp8 per-tensor scales (device), else null
+  const float* dy_scale;
+  int64_t T, N, K;
+};
+
+// Launchers (defined in the .hip translation units).  Return a hipError_t as int.
+int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmArgs& g, const EpiArgs& e,
+                      void* stream);
+int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream);
+int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n_elem, const EpiArgs& e,
+                     void* stream);
+int launch_dgrad(const void* dY, const void* W, void* dX, int64_t T, int64_t N, int64_t K, void* stream);
+
+}  // namespace forge

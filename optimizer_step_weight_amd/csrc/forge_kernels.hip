@@ -1,0 +1,263 @@
+// forge_kernels.hip -- kernels and launchers of the fused and the unfused paths.
+//
+// Fused (FORGE explainer, gist.science, Technical Summary section 2 "Core Mechanism"): one
+// workgroup per 128 x 128 tile of W contracts dY and X over all tokens into fp32
+// accumulators, then applies the optimizer to the tile and writes back only W and its
+// moments.  The gradient tile lives in registers and, for the re-layout to 16 consecutive
+// columns per thread, in the workgroup's LDS; it never reaches HBM.
+//
+// Unfused baseline (Technical Summary section 1 "The Problem"): the same contraction writes
+// the fp32 gradient to HBM, and a separate element-wise kernel reads it back and applies the
+// same update code.
+//
+// dgrad: dX = dY W, run before the step so that it sees the old weight (Technical Summary
+// section 5, limitations).
+#include <hip/hip_runtime.h>
+
+#include "forge_mainloop.h"
+
+namespace forge {
+
+template <int IN>
+__device__ __forceinline__ float input_scale(const GemmArgs& g) {
+  if constexpr (IN == FORGE_IN_FP8) return g.dy_scale[0] * g.x_scale[0];
+  return 1.0f;
+}
+
+template <int IN, int WT, int ST, int OPT>
+__global__ __launch_bounds__(kThreads, 2) void fused_step_kernel(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  const int nbN = (int)(g.N / kBM), nbK = (int)(g.K / kBN);
+  int nb, kb;
+  tile_coords(nbN, nbK, nb, kb);
+  const int n0 = nb * kBM, k0 = kb * kBN;
+
+  floatx4 acc[4][4];
+  contract_tile<IN>(acc, smem, g, n0, k0);
+
+  float* st = reinterpret_cast<float*>(smem);
+  stage_acc(st, acc, input_scale<IN>(g));
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int s = 0; s < 4; ++s) {
+    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
+    float gr[16];
+    read_seg16(gr, st, row, kseg);
+    const uint32_t i0 = (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+    step_segment16<OPT, WT, ST>(gr, i0, e);
+  }
+}
+
+template <int IN>
+__global__ __launch_bounds__(kThreads, 2) void wgrad_gemm_kernel(GemmArgs g, float* dW) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  const int nbN = (int)(g.N / kBM), nbK = (int)(g.K / kBN);
+  int nb, kb;
+  tile_coords(nbN, nbK, nb, kb);
+  const int n0 = nb * kBM, k0 = kb * kBN;
+
+  floatx4 acc[4][4];
+  contract_tile<IN>(acc, smem, g, n0, k0);
+
+  float* st = reinterpret_cast<float*>(smem);
+  stage_acc(st, acc, input_scale<IN>(g));
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
+    const float* p = st + row * kEpiLd + kseg * 16;
+    float* d = dW + (int64_t)(n0 + row) * g.K + k0 + kseg * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
+  }
+}
+
+// Element-wise rule over a materialised gradient: one thread per 16 consecutive elements.
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t nseg, EpiArgs e) {
+  const int64_t seg = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (seg >= nseg) return;  // nseg % 4 == 0, so the 4 lanes of an int8 block leave together
+  float g[16];
+  const float* p = dW + seg * 16;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 x = ld16(p + 4 * q);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[4 * q + c] = __uint_as_float(x[c]);
+  }
+  step_segment16<OPT, WT, ST>(g, (uint32_t)(seg * 16), e);
+}
+
+// dX[T, K] = dY[T, N] . W[N, K], bf16 in, fp32 accumulate, bf16 (nearest-even) out.
+// Tile 128 tokens x 128 columns; the reduction runs over N in slabs of 64.  The dY slab is
+// already reduction-contiguous and is copied to LDS as is; the W slab is transposed into
+// [k][n] rows like the wgrad panels.
+__global__ __launch_bounds__(kThreads, 2) void dgrad_kernel(const uint16_t* dY, const uint16_t* W, uint16_t* dX,
+                                                            int64_t T, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  const int nbK = (int)(K / kBN);
+  const int tb = blockIdx.x / nbK, kb = blockIdx.x % nbK;
+  const int64_t t0 = (int64_t)tb * 128;
+  const int k0 = kb * kBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int op = tid >> 7, lt = tid & 127;
+  // dY role: rows (lt >> 3) + 16 i of the 128-token tile, 16-byte chunk (lt & 7) of the 64-wide slab
+  // W role: rows 8 (lt % 8) + i of the 64-row slab, 16-byte chunk lt / 8 of the 128 columns
+  const int rg = lt & 7, ch = lt >> 3;
+  const int nsl = (int)(N / 64);
+  u32x4 buf[8];
+  auto load = [&](int s) {
+    const int64_t nbase = (int64_t)s * 64;
+    if (op == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = t0 + (lt >> 3) + 16 * i;
+        buf[i] = t < T ? ld16(dY + t * N + nbase + (lt & 7) * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) buf[i] = ld16(W + (nbase + rg * 8 + i) * K + k0 + ch * 8);
+    }
+  };
+  auto store = [&](unsigned char* stage) {
+    if (op == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(stage + ((lt >> 3) + 16 * i) * kLdsRow + (lt & 7) * 16) = buf[i];
+    } else {
+      store_transposed<FORGE_IN_BF16>(stage + kPanel, buf, ch, rg);
+    }
+  };
+  if (nsl > 0) {  // N == 0 leaves dX = 0
+    load(0);
+    store(smem);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsl; ++s) {
+    unsigned char* stage = smem + (s & 1) * kStage;
+    if (s + 1 < nsl) load(s + 1);
+    mma_slab<FORGE_IN_BF16>(acc, stage + wm * 64 * kLdsRow, stage + kPanel + wn * 64 * kLdsRow, lane);
+    if (s + 1 < nsl) store(smem + ((s + 1) & 1) * kStage);
+    __syncthreads();
+  }
+  float* st = reinterpret_cast<float*>(smem);
+  stage_acc(st, acc, 1.0f);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
+    const int64_t t = t0 + row;
+    if (t >= T) continue;
+    float gr[16];
+    read_seg16(gr, st, row, kseg);
+    u32x4 a, b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
+      b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
+    }
+    uint16_t* d = dX + t * K + k0 + kseg * 16;
+    st16(d, a);
+    st16(d + 8, b);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch tables
+using FusedFn = void (*)(GemmArgs, EpiArgs);
+using OptFn = void (*)(const float*, int64_t, EpiArgs);
+
+template <int IN, int WT, int ST>
+static FusedFn fused_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return fused_step_kernel<IN, WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return fused_step_kernel<IN, WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return fused_step_kernel<IN, WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return fused_step_kernel<IN, WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return fused_step_kernel<IN, WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return fused_step_kernel<IN, WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return fused_step_kernel<IN, WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return fused_step_kernel<IN, WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
+
+template <int IN>
+static FusedFn fused_for(int w, int s, int opt) {
+  if (w == FORGE_W_BF16) return s == FORGE_S_F32 ? fused_for<IN, FORGE_W_BF16, FORGE_S_F32>(opt)
+                                                 : fused_for<IN, FORGE_W_BF16, FORGE_S_Q8>(opt);
+  return s == FORGE_S_F32 ? fused_for<IN, FORGE_W_F32, FORGE_S_F32>(opt) : fused_for<IN, FORGE_W_F32, FORGE_S_Q8>(opt);
+}
+
+template <int WT, int ST>
+static OptFn opt_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return optimizer_kernel<WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return optimizer_kernel<WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return optimizer_kernel<WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return optimizer_kernel<WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return optimizer_kernel<WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return optimizer_kernel<WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return optimizer_kernel<WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return optimizer_kernel<WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
+
+int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmArgs& g, const EpiArgs& e,
+                      void* stream) {
+  FusedFn fn = nullptr;
+  if (in_type == FORGE_IN_BF16) fn = fused_for<FORGE_IN_BF16>(w_type, s_type, opt);
+  else if (in_type == FORGE_IN_F32) fn = fused_for<FORGE_IN_F32>(w_type, s_type, opt);
+  else if (in_type == FORGE_IN_FP8) fn = fused_for<FORGE_IN_FP8>(w_type, s_type, opt);
+  if (!fn) return (int)hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, e);
+  return (int)hipGetLastError();
+}
+
+int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
+  const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));
+  if (in_type == FORGE_IN_BF16)
+    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_BF16>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
+  else if (in_type == FORGE_IN_F32)
+    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_F32>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
+  else if (in_type == FORGE_IN_FP8)
+    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_FP8>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n_elem, const EpiArgs& e,
+                     void* stream) {
+  OptFn fn;
+  if (w_type == FORGE_W_BF16)
+    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_BF16, FORGE_S_F32>(opt) : opt_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+  else
+    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_F32, FORGE_S_F32>(opt) : opt_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+  if (!fn) return (int)hipErrorInvalidValue;
+  const int64_t nseg = n_elem / 16;
+  const unsigned grid = (unsigned)((nseg + 255) / 256);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, dW, nseg, e);
+  return (int)hipGetLastError();
+}
+
+int launch_dgrad(const void* dY, const void* W, void* dX, int64_t T, int64_t N, int64_t K, void* stream) {
+  const unsigned grid = (unsigned)(((T + 127) / 128) * (K / kBN));
+  hipLaunchKernelGGL(dgrad_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(dX), T,
+                     N, K);
+  return (int)hipGetLastError();
+}
+
+}  // namespace forge

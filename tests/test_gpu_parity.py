@@ -1,0 +1,319 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case prints what identifies it before touching the GPU.  Shapes span several 128 x 128
+tiles and a ragged final token slab (T = 200 is not a multiple of the 32 / 64 / 128-token
+slabs of the fp32 / bf16 / fp8 mainloops).
+
+Protocols (see tests/parity.py for the acceptance rules):
+  * exact-sum inputs, oracle-fed: before each step the device state is set to the oracle's
+    stored state after the previous step, so each step is compared on identical inputs;
+  * exact-sum inputs, free-running: the device keeps its own state for several steps;
+  * Gaussian inputs with the workloads' standard deviations: the envelope over the fp32
+    summation error bound of the gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import numerics, optimizers, wgrad
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+N, K, T = 256, 384, 200
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import optimizer_step_weight_amd as forge
+    if not __import__("os").path.exists(forge.LIB_PATH):
+        from optimizer_step_weight_amd import _build
+        _build.build(verbose=False)
+    forge.device_check(0)
+    return forge
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _init_states(opt, state_fmt, rng, N=N, K=K):
+    """Non-trivial previous moments in the rule's domain (v >= 0)."""
+    m, v = wgrad.init_states(opt, N, K, state_fmt)
+    mm = rng.standard_normal((N, K)) * 2e-3
+    vv = np.abs(rng.standard_normal((N, K))) * 1e-5
+    if opt == "adagrad":
+        vv = vv * 10
+    if state_fmt == "f32":
+        m = None if m is None else mm.astype(np.float32)
+        v = None if v is None else vv.astype(np.float32)
+    else:
+        m = None if m is None else numerics.quantize_block64(mm, True)
+        v = None if v is None else numerics.quantize_block64(vv, False)
+    return m, v
+
+
+def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, lo=None, hi=None, tag=""):
+    P.weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W")
+    if pre is not None:
+        P.preround_close(pre, ref["W64"] if lo is None else lo, ref["W64"] if hi is None else hi, what=f"{tag} W32")
+    P.state_close(got_m, ref["m"], ref["m64"], state_fmt, f"{tag} m")
+    P.state_close(got_v, ref["v"], ref["v64"], state_fmt, f"{tag} v")
+
+
+EXACT = [(opt, i, w, s) for opt in synth.OPTIMIZERS
+         for (i, w) in (("bf16", "bf16"), ("f32", "f32"), ("fp8", "bf16"), ("bf16", "f32"))
+         for s in ("f32", "int8")]
+
+
+@pytest.mark.parametrize("opt,in_fmt,w_fmt,state_fmt", EXACT, ids=["-".join(c) for c in EXACT])
+def test_fused_step_exact_inputs_oracle_fed(lib, opt, in_fmt, w_fmt, state_fmt):
+    rng = np.random.default_rng(abs(hash((opt, in_fmt, w_fmt, state_fmt))) % 2 ** 32)
+    h = synth.default_hyper(opt)
+    seed = 1234 + synth.OPTIMIZERS.index(opt)
+    W = synth.random_weight(7, N, K, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng)
+    for i, t in enumerate((1, 2, 7)):
+        _say("exact oracle-fed", opt, in_fmt, w_fmt, state_fmt, "step", t)
+        X, dY = synth.integer_case(100 * i + 3, T, N, K, in_fmt)
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, seed, w_fmt, state_fmt)
+        d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, seed, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, tag=f"step {t}")
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+FREE = [("adamw", "bf16", "bf16"), ("lion", "bf16", "bf16"), ("nadam", "fp8", "bf16"), ("sgd_momentum", "f32", "f32"),
+        ("radam", "bf16", "bf16"), ("rmsprop", "bf16", "f32"), ("adagrad", "bf16", "bf16"), ("sgd", "fp8", "bf16")]
+
+
+@pytest.mark.parametrize("opt,in_fmt,w_fmt", FREE, ids=["-".join(c) for c in FREE])
+def test_fused_free_running_exact_inputs(lib, opt, in_fmt, w_fmt):
+    """The device keeps its own W, m, v over 7 steps (fp32 moments)."""
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(9, N, K, w_fmt)
+    m, v = wgrad.init_states(opt, N, K, "f32")
+    d = P.DeviceStep(W, m, v, w_fmt, "f32")
+    for t in range(1, 8):
+        _say("exact free-running", opt, in_fmt, w_fmt, "step", t)
+        X, dY = synth.integer_case(500 + t, T, N, K, in_fmt)
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 77, w_fmt, "f32")
+        d.fused(lib, X, dY, opt, h, t, 77)
+        gW, gm, gv = d.host()
+        if w_fmt == "bf16":
+            dist = P.ulp_distance(gW, ref["W"])
+            assert dist.max() <= 1, f"step {t}: {int((dist > 1).sum())} weights more than 1 ULP away"
+        else:
+            P.weight_close(gW, ref, w_fmt, what=f"step {t} W")
+        P.state_close(gm, ref["m"], ref["m64"], "f32", f"step {t} m")
+        P.state_close(gv, ref["v"], ref["v64"], "f32", f"step {t} v")
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+GAUSS = ([(opt, "bf16", "bf16", "f32") for opt in synth.OPTIMIZERS]
+         + [("adamw", "bf16", "bf16", "int8"), ("adamw", "fp8", "bf16", "f32"), ("lion", "fp8", "bf16", "f32"),
+            ("adamw", "f32", "f32", "f32"), ("rmsprop", "bf16", "bf16", "int8")])
+
+
+@pytest.mark.parametrize("opt,in_fmt,w_fmt,state_fmt", GAUSS, ids=["-".join(c) for c in GAUSS])
+def test_fused_step_gaussian_envelope(lib, opt, in_fmt, w_fmt, state_fmt):
+    rng = np.random.default_rng(5)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(11, N, K, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng)
+    for i, t in enumerate((1, 3, 6)):
+        _say("gaussian envelope", opt, in_fmt, w_fmt, state_fmt, "step", t)
+        X, dY = synth.gaussian_case(40 + i, T, N, K, in_fmt)
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 99, w_fmt, state_fmt)
+        tau = P.grad_bound(X, dY)
+        lo, hi = P.envelope(opt, h, t, ref["g"], tau, W, m, v, w_fmt, state_fmt)
+        d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, 99, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, lo, hi, tag=f"step {t}")
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+UNF = [(opt, "bf16", "bf16", "f32") for opt in synth.OPTIMIZERS] + [
+    ("adamw", "bf16", "bf16", "int8"), ("adamw", "fp8", "bf16", "f32"), ("adamw", "f32", "f32", "f32"),
+    ("lion", "bf16", "f32", "int8")]
+
+
+@pytest.mark.parametrize("opt,in_fmt,w_fmt,state_fmt", UNF, ids=["-".join(c) for c in UNF])
+def test_fused_equals_unfused_bitwise(lib, opt, in_fmt, w_fmt, state_fmt):
+    """Same contraction, same rule code: the two schedules give identical bits (exactness claim)."""
+    _say("fused vs unfused", opt, in_fmt, w_fmt, state_fmt)
+    rng = np.random.default_rng(8)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(12, N, K, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng)
+    X, dY = synth.gaussian_case(60, T, N, K, in_fmt)
+    a = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+    b = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+    pa = a.fused(lib, X, dY, opt, h, 4, 5, preround=True)
+    pb, dW = b.unfused(lib, X, dY, opt, h, 4, 5, preround=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
+    for x, y in zip(a.host(), b.host()):
+        if x is None:
+            assert y is None
+        elif isinstance(x, tuple):
+            assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+        else:
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("in_fmt", ["bf16", "f32", "fp8"])
+def test_wgrad_gemm_matches_oracle(lib, in_fmt):
+    _say("wgrad gemm", in_fmt)
+    X, dY = synth.integer_case(70, T, N, K, in_fmt)
+    dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    Xd, xs = P.dev_operand(X)
+    Dd, ds = P.dev_operand(dY)
+    lib.wgrad_gemm(Xd, Dd, dW, x_scale=xs, dy_scale=ds)
+    ref = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    np.testing.assert_array_equal(dW.cpu().numpy().astype(np.float64), ref)      # exact sums: bitwise
+    X, dY = synth.gaussian_case(71, T, N, K, in_fmt)
+    Xd, xs = P.dev_operand(X)
+    Dd, ds = P.dev_operand(dY)
+    lib.wgrad_gemm(Xd, Dd, dW, x_scale=xs, dy_scale=ds)
+    ref = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    err = np.abs(dW.cpu().numpy().astype(np.float64) - ref)
+    tau = P.grad_bound(X, dY)
+    assert np.all(err <= tau), float(np.max(err / np.maximum(tau, 1e-300)))
+    print(f"  max |err| / bound = {float(np.max(err / np.maximum(tau, 1e-300))):.3e}")
+
+
+@pytest.mark.parametrize("Tn,Nn,Kn", [(200, 256, 384), (128, 384, 256), (1, 128, 128), (333, 640, 128)])
+def test_dgrad_matches_oracle(lib, Tn, Nn, Kn):
+    _say("dgrad", Tn, Nn, Kn)
+    # exact sums: dY and W on a dyadic grid
+    _, dY = synth.integer_case(80, Tn, Nn, 128, "bf16")
+    Wi, _ = synth.integer_case(81, Nn, 128, Kn, "bf16")      # X-shaped [Nn, Kn] grid values in [-1, 1]
+    Wd = P.dev_weight(Wi.data, "bf16")
+    dYd, _ = P.dev_operand(dY)
+    dX = torch.empty((Tn, Kn), dtype=torch.bfloat16, device="cuda")
+    lib.dgrad(dYd, Wd, dX)
+    ref = wgrad.dgrad_bf16(wgrad.decode_operand(dY), numerics.bf16_to_f64(Wi.data))
+    got = dX.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    # Gaussian: bf16 nearest-even of an fp32 sum, within 1 ULP of the oracle's rounding
+    _, dY = synth.gaussian_case(82, Tn, Nn, 128, "bf16")
+    W = synth.random_weight(83, Nn, Kn, "bf16")
+    dYd, _ = P.dev_operand(dY)
+    lib.dgrad(dYd, P.dev_weight(W, "bf16"), dX)
+    ref = wgrad.dgrad_bf16(wgrad.decode_operand(dY), numerics.bf16_to_f64(W))
+    got = dX.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert P.ulp_distance(got, ref).max() <= 1
+
+
+def test_backward_step_reads_the_old_weight(lib):
+    """dX must see W before the update (limitation stated in the explainer's section 5)."""
+    _say("ordering")
+    X, dY = synth.gaussian_case(90, T, N, K, "bf16")
+    W = synth.random_weight(91, N, K, "bf16")
+    m, v = wgrad.init_states("adamw", N, K, "f32")
+    h = synth.Hyper(lr=0.05, weight_decay=0.0)   # large steps make the order visible
+    d = P.DeviceStep(W, m, v, "bf16", "f32")
+    Xd, _ = P.dev_operand(X)
+    dYd, _ = P.dev_operand(dY)
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    lib.linear_backward_step(Xd, dYd, d.W, dX, d.m, d.v, opt="adamw", hyper=h, step=1, seed=3)
+    got = dX.view(torch.int16).cpu().numpy().view(np.uint16)
+    dY64 = wgrad.decode_operand(dY)
+    old = wgrad.dgrad_bf16(dY64, numerics.bf16_to_f64(W))
+    assert P.ulp_distance(got, old).max() <= 1
+    ref = wgrad.step(X, dY, W, m, v, "adamw", h, 1, 3, "bf16", "f32")
+    new = wgrad.dgrad_bf16(dY64, numerics.bf16_to_f64(ref["W"]))
+    assert P.ulp_distance(got, new).max() > 1          # the reversed order is visibly different
+    P.weight_close(d.host()[0], ref, "bf16", *P.envelope("adamw", h, 1, ref["g"], P.grad_bound(X, dY), W, m, v,
+                                                         "bf16", "f32"))
+
+
+@pytest.mark.parametrize("Tn", [0, 1, 64, 65])
+def test_edge_token_counts(lib, Tn):
+    _say("edge T", Tn)
+    h = synth.default_hyper("adamw")
+    X, dY = synth.integer_case(95, Tn, N, K, "bf16")
+    W = synth.random_weight(96, N, K, "bf16")
+    m, v = wgrad.init_states("adamw", N, K, "f32")
+    ref = wgrad.step(X, dY, W, m, v, "adamw", h, 1, 4, "bf16", "f32")
+    d = P.DeviceStep(W, m, v, "bf16", "f32")
+    pre = d.fused(lib, X, dY, "adamw", h, 1, 4, preround=True)
+    gW, gm, gv = d.host()
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32")
+    if Tn == 0:  # zero gradient: pure decoupled decay
+        np.testing.assert_allclose(pre.cpu().numpy(), numerics.bf16_to_f64(W) * (1 - np.float32(1e-3) * np.float32(0.01)),
+                                   rtol=1e-6)
+
+
+def test_empty_weight_is_a_no_op(lib):
+    _say("empty N")
+    X = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    dY = torch.zeros((64, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    lib.wgrad_step(X, dY, W, torch.zeros((0, 128), device="cuda"), torch.zeros((0, 128), device="cuda"),
+                   opt="adamw", hyper=synth.default_hyper("adamw"), step=1, seed=1)
+    torch.cuda.synchronize()
+
+
+def test_determinism_and_resume(lib):
+    """Same inputs, seed and step give the same bits; 5 steps straight == 2 + host round trip + 3."""
+    _say("determinism / resume")
+    h = synth.default_hyper("adamw")
+    W0 = synth.random_weight(20, N, K, "bf16")
+    m0, v0 = wgrad.init_states("adamw", N, K, "f32")
+    ins = [synth.gaussian_case(200 + t, T, N, K, "bf16") for t in range(1, 6)]
+    a = P.DeviceStep(W0, m0, v0, "bf16", "f32")
+    for t in range(1, 6):
+        a.fused(lib, *ins[t - 1], "adamw", h, t, 42)
+    b = P.DeviceStep(W0, m0, v0, "bf16", "f32")
+    for t in range(1, 3):
+        b.fused(lib, *ins[t - 1], "adamw", h, t, 42)
+    Wb, mb, vb = b.host()
+    c = P.DeviceStep(Wb, mb, vb, "bf16", "f32")
+    for t in range(3, 6):
+        c.fused(lib, *ins[t - 1], "adamw", h, t, 42)
+    for x, y in zip(a.host(), c.host()):
+        assert np.array_equal(x, y)
+    a2 = P.DeviceStep(W0, m0, v0, "bf16", "f32")
+    for t in range(1, 6):
+        a2.fused(lib, *ins[t - 1], "adamw", h, t, 42)
+    for x, y in zip(a.host(), a2.host()):
+        assert np.array_equal(x, y)
+
+
+def test_stochastic_rounding_escapes_the_dead_zone(lib):
+    """Sub-ULP updates: nearest-even leaves W frozen, stochastic rounding tracks the fp32 sum."""
+    _say("dead zone")
+    n, k, steps = 256, 256, 40
+    X = torch.zeros((64, k), dtype=torch.bfloat16, device="cuda")
+    X[0, :] = 1.0
+    dY = torch.zeros((64, n), dtype=torch.bfloat16, device="cuda")
+    dY[0, :] = 1.0                                   # g = 1 everywhere
+    w0 = 0.02
+    ulp = float(P.bf16_ulp(numerics.bf16_rne(np.array([w0], np.float32)))[0])
+    lr = 0.1 * ulp                                   # SGD: each step moves W by 0.1 ULP
+    h = synth.Hyper(lr=lr)
+    W_rne = torch.full((n, k), w0, dtype=torch.bfloat16, device="cuda")
+    W_sr = W_rne.clone()
+    start = float(W_rne[0, 0])
+    for t in range(1, steps + 1):
+        lib.wgrad_step(X, dY, W_rne, opt="sgd", hyper=h, step=t, seed=5, sr=False)
+        lib.wgrad_step(X, dY, W_sr, opt="sgd", hyper=h, step=t, seed=5)
+    torch.cuda.synchronize()
+    assert torch.all(W_rne == start)
+    drift = W_sr.double().cpu().numpy() - start
+    want = -steps * float(np.float32(lr))
+    sd = ulp * np.sqrt(steps * 0.25) / np.sqrt(n * k)
+    assert abs(drift.mean() - want) < 6 * sd + 1e-3 * abs(want), (drift.mean(), want)
+    # and it equals the oracle's stream, element by element, for the first step
+    Wb = numerics.bf16_rne(np.full((n, k), w0, np.float32))
+    Xo = synth.Operand("bf16", X.view(torch.int16).cpu().numpy().view(np.uint16))
+    Do = synth.Operand("bf16", dY.view(torch.int16).cpu().numpy().view(np.uint16))
+    ref = wgrad.step(Xo, Do, Wb, None, None, "sgd", h, 1, 5, "bf16", "f32")
+    Wg = P.dev_weight(Wb, "bf16")
+    lib.wgrad_step(X, dY, Wg, opt="sgd", hyper=h, step=1, seed=5)
+    np.testing.assert_array_equal(P.host_weight(Wg, "bf16"), ref["W"])
