@@ -261,6 +261,10 @@ static forge_status validate_inputs(const forge_tensor* X, const forge_tensor* d
     ins[n++] = range_of(X->scale, 4, "X scale");
     ins[n++] = range_of(dY->scale, 4, "dY scale");
   }
+  // the kernels address X and dY with 32-bit byte offsets (one spare slab of tokens included)
+  const int64_t esz = dtype_size(X->dtype);
+  if ((X->rows + 128) * X->cols * esz >= (int64_t(1) << 32) || (dY->rows + 128) * dY->cols * esz >= (int64_t(1) << 32))
+    return fail(FORGE_ERR_SHAPE, "X and dY must each stay below 4 GiB");
   g->X = X->data;
   g->dY = dY->data;
   g->T = X->rows;

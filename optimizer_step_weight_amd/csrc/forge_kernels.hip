@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include "forge_mainloop.h"
+#include "forge_mainloop2.h"
 
 namespace forge {
 
@@ -72,6 +73,63 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_gemm_kernel(GemmArgs g, flo
 #pragma unroll
     for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
   }
+}
+
+// bf16 inputs, 256 x 128 workgroup tiles fed by LDS DMA (forge_mainloop2.h).
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(ml2::THREADS, 1) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[ml2::SMEM];
+  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+  int nb, kb;
+  tile_coords(nbN, nbK, nb, kb);
+  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract(acc, smem, g, n0, k0);
+  float* st = reinterpret_cast<float*>(smem);
+  ml2::stage_acc(st, acc, 1.0f);
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int s = 0; s < 8; ++s) {
+    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
+    float gr[16];
+    const float* p = st + row * ml2::EPI_LD + kseg * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+    }
+    const uint32_t i0 = (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+    step_segment16<OPT, WT, ST>(gr, i0, e);
+  }
+}
+
+__global__ __launch_bounds__(ml2::THREADS, 1) void wgrad_gemm_kernel2(GemmArgs g, float* dW) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[ml2::SMEM];
+  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+  int nb, kb;
+  tile_coords(nbN, nbK, nb, kb);
+  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract(acc, smem, g, n0, k0);
+  float* st = reinterpret_cast<float*>(smem);
+  ml2::stage_acc(st, acc, 1.0f);
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
+    const float* p = st + row * ml2::EPI_LD + kseg * 16;
+    float* d = dW + (int64_t)(n0 + row) * g.K + k0 + kseg * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
+  }
+}
+
+// The 256 x 128 path needs N % 256 == 0 and enough tiles to give every CU one.
+static bool use_v2(int in_type, const GemmArgs& g) {
+  return in_type == FORGE_IN_BF16 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
 }
 
 // Element-wise rule over a materialised gradient: one thread per 16 consecutive elements.
@@ -176,6 +234,21 @@ __global__ __launch_bounds__(kThreads, 2) void dgrad_kernel(const uint16_t* dY, 
 using FusedFn = void (*)(GemmArgs, EpiArgs);
 using OptFn = void (*)(const float*, int64_t, EpiArgs);
 
+template <int WT, int ST>
+static FusedFn fused2_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return fused_step_kernel2<WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return fused_step_kernel2<WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return fused_step_kernel2<WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return fused_step_kernel2<WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return fused_step_kernel2<WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return fused_step_kernel2<WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return fused_step_kernel2<WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return fused_step_kernel2<WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
+
 template <int IN, int WT, int ST>
 static FusedFn fused_for(int opt) {
   switch (opt) {
@@ -216,6 +289,16 @@ static OptFn opt_for(int opt) {
 int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmArgs& g, const EpiArgs& e,
                       void* stream) {
   FusedFn fn = nullptr;
+  if (use_v2(in_type, g)) {
+    if (w_type == FORGE_W_BF16)
+      fn = s_type == FORGE_S_F32 ? fused2_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused2_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+    else
+      fn = s_type == FORGE_S_F32 ? fused2_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused2_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const unsigned grid2 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
+    hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, e);
+    return (int)hipGetLastError();
+  }
   if (in_type == FORGE_IN_BF16) fn = fused_for<FORGE_IN_BF16>(w_type, s_type, opt);
   else if (in_type == FORGE_IN_F32) fn = fused_for<FORGE_IN_F32>(w_type, s_type, opt);
   else if (in_type == FORGE_IN_FP8) fn = fused_for<FORGE_IN_FP8>(w_type, s_type, opt);
@@ -226,6 +309,11 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
 }
 
 int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
+  if (use_v2(in_type, g)) {
+    const unsigned grid2 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
+    hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, dW);
+    return (int)hipGetLastError();
+  }
   const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));
   if (in_type == FORGE_IN_BF16)
     hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_BF16>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);

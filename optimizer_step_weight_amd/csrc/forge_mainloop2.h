@@ -1,0 +1,191 @@
+// forge_mainloop2.h -- token contraction of a 256 x 128 weight tile (two 128 x 128 tiles of
+// the method) for bf16 inputs, fed by direct global->LDS DMA and LDS transpose reads.
+//
+// FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism": the tile's
+// gradient dW[n, k] = sum_t dY[t, n] X[t, k] is accumulated over all tokens in fp32
+// registers.  Any order of the tokens is a valid summation order (section 2 "Precision and
+// Fidelity"), so the token <-> MFMA k-slot assignment only has to be the same for dY and X.
+//
+// Data path (gfx950):
+//  * A slab of 64 tokens of dY[:, n0:n0+256] (32 KiB) and X[:, k0:k0+128] (16 KiB) is
+//    copied to LDS by buffer_load_dwordx4 ... lds: every lane moves 16 bytes and the wave's
+//    64 lanes fill 1 KiB of LDS in lane order.  Rows stay token-major, exactly as in HBM.
+//    Tokens past T read as zero (buffer range check), so a ragged last slab needs no code.
+//  * Three slabs are in flight (3 x 48 KiB of LDS); the copy of slab s+2 is issued while
+//    slab s is multiplied.
+//  * The MFMA operands need 8 tokens of one n (or k) per lane.  ds_read_b64_tr_b16 gives
+//    exactly that from token-major rows: within each group of 16 lanes, lane j receives
+//    element (j % 4) of the 8-byte piece addressed by lane 4 f + j / 4, for f = 0..3.  Lane
+//    i of a group therefore points at token row (base + i / 4), columns (c0 + 4 (i % 4)) ..
+//    +3, and lane j gets tokens base..base+3 of column c0 + j.
+//  * 16-byte chunks of a token row are XOR-swizzled with 2 * (t mod 8), chosen through the
+//    global address each DMA lane fetches; the transpose reads of 8 consecutive token rows
+//    then hit 8 disjoint bank groups.
+//
+// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k), wave tile 128 x 64 = 8 x 4 MFMA
+// 16x16x32 blocks (128 accumulator registers per lane), one workgroup per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "forge_device.h"
+
+namespace forge {
+namespace ml2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define FORGE_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int BM = 256, BN = 128, TK = 64, STAGES = 3, THREADS = 256;
+constexpr int ROW_A = BM * 2;          // bytes per dY token row in LDS (512)
+constexpr int ROW_B = BN * 2;          // bytes per X token row (256)
+constexpr int PANEL_A = TK * ROW_A;    // 32 KiB
+constexpr int PANEL_B = TK * ROW_B;    // 16 KiB
+constexpr int STAGE = PANEL_A + PANEL_B;
+constexpr int SMEM = STAGES * STAGE;   // 147456 bytes
+constexpr int EPI_LD = BN + 4;         // fp32 staging row stride (floats): 256 x 132 x 4 = 135168 bytes
+static_assert(BM * EPI_LD * 4 <= SMEM, "epilogue staging must fit in the stage buffers");
+
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 7); }
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64); lgkm and exp at max.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Barrier that orders LDS use between the waves without waiting for outstanding DMA.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes, default format word.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// One 16-byte-per-lane copy global -> LDS (lane l lands at lds + 16 l).  Issued as inline asm
+// so that the compiler does not add a wait for it before every LDS read (it cannot prove the
+// copy and the reads touch different stages); completion is awaited explicitly with wait_vm.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, const unsigned char* lds) {
+  const uint32_t la =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(la), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+struct Feed {
+  u32x4 rA, rB;                   // dY and X as buffer resources (out-of-range reads give 0)
+  uint32_t offA[8], offB[4];      // per-lane byte offsets of this wave's DMA pieces, token 0
+  uint32_t stepA, stepB;          // bytes per slab (TK rows)
+};
+
+// Per-lane DMA offsets.  Wave w moves dY rows 2 d, 2 d + 1 (d = 8 w + j, j < 8) and X rows
+// 4 x .. 4 x + 3 (x = 4 w + j, j < 4) of every slab.
+__device__ __forceinline__ void make_feed(Feed& f, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+                                          int n0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(dY, (uint32_t)(T * N * 2));
+  f.rB = make_rsrc(X, (uint32_t)(T * K * 2));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = 8 * wave + j, r = 2 * d + (lane >> 5), p = lane & 31;
+    const int c = p ^ swz(r);
+    f.offA[j] = (uint32_t)(r * N * 2 + n0 * 2 + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = 4 * wave + j, r = 4 * x + (lane >> 4), p = lane & 15;
+    const int c = p ^ swz(r);
+    f.offB[j] = (uint32_t)(r * K * 2 + k0 * 2 + c * 16);
+  }
+  f.stepA = (uint32_t)(TK * N * 2);
+  f.stepB = (uint32_t)(TK * K * 2);
+}
+
+__device__ __forceinline__ void issue(const Feed& f, unsigned char* stage, int slab) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma16(f.rA, f.offA[j] + sa, stage + (8 * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(f.rB, f.offB[j] + sb, stage + PANEL_A + (4 * wave + j) * 1024);
+}
+
+// Byte offset (within a panel) of this lane's transpose-read piece for 16 columns starting at
+// c0, token rows base + (lane % 16) / 4 of a 32-token step.
+__device__ __forceinline__ int tr_off(int row_bytes, int row, int c0, int i) {
+  const int c = (c0 >> 3) + ((i & 3) >> 1);
+  return row * row_bytes + 16 * (c ^ swz(row)) + 8 * (i & 1);
+}
+
+__device__ __forceinline__ bf16x8 frag(const unsigned char* panel, int row_bytes, int r0, int r1, int c0, int i) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FORGE_LDS(v4i16, panel + tr_off(row_bytes, r0, c0, i)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FORGE_LDS(v4i16, panel + tr_off(row_bytes, r1, c0, i)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+__device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + PANEL_A;
+#pragma unroll
+  for (int kk = 0; kk < TK / 32; ++kk) {
+    const int r0 = 32 * kk + 4 * q + (i >> 2), r1 = r0 + 16;
+    bf16x8 b[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, ROW_B, r0, r1, wn * 64 + 16 * bj, i);
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi) {
+      const bf16x8 a = frag(pa, ROW_A, r0, r1, wm * 128 + 16 * bi, i);
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
+    }
+  }
+}
+
+// acc = dW of tile (n0, k0) over all T tokens.  Ends with a barrier (LDS free for reuse).
+__device__ __forceinline__ void contract(floatx4 (&acc)[8][4], unsigned char* smem, const GemmArgs& g, int n0,
+                                         int k0) {
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  Feed f;
+  make_feed(f, g.dY, g.X, g.T, g.N, g.K, n0, k0);
+  const int nsl = (int)((g.T + TK - 1) / TK);
+  if (nsl > 0) issue(f, smem, 0);
+  if (nsl > 1) issue(f, smem + STAGE, 1);
+  for (int s = 0; s < nsl; ++s) {
+    if (s + 1 < nsl) wait_vm<12>();
+    else wait_vm<0>();
+    barrier();
+    if (s + 2 < nsl) issue(f, smem + ((s + 2) % STAGES) * STAGE, s + 2);
+    mma_stage(acc, smem + (s % STAGES) * STAGE, wm, wn);
+  }
+  barrier();
+}
+
+__device__ __forceinline__ void stage_acc(float* st, const floatx4 (&acc)[8][4], float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        st[(wm * 128 + 16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
+}
+
+}  // namespace ml2
+}  // namespace forge

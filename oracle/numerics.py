@@ -72,6 +72,25 @@ def sr_bits(seed: int, step: int, idx: np.ndarray) -> np.ndarray:
     return ((word >> sh) & np.uint64(0xFFFF)).astype(np.uint16)
 
 
+def sr_bits_block(seed: int, step: int, row0: int, col0: int, rows: int, cols: int, K: int) -> np.ndarray:
+    """sr_bits for the [rows, cols] block of a row-major [., K] weight at (row0, col0).
+
+    Same values as sr_bits on the block's flat indices; requires col0 and cols to be
+    multiples of 16 so that every 16-element Philox block lies inside the block, and draws
+    each Philox block once.
+    """
+    assert col0 % 16 == 0 and cols % 16 == 0 and K % 16 == 0
+    rr = np.arange(rows, dtype=np.uint64)[:, None] + np.uint64(row0)
+    bb = np.arange(cols // 16, dtype=np.uint64)[None, :] + np.uint64(col0 // 16)
+    blk = (rr * np.uint64(K // 16) + bb).reshape(-1)
+    w = philox4x64_10(blk, np.uint64(step), np.uint64(0), np.uint64(0),
+                      np.uint64(seed & 0xFFFFFFFFFFFFFFFF), np.uint64(0))
+    words = np.stack(w, axis=1)                                     # [blocks, 4] uint64
+    parts = [(words >> np.uint64(16 * f)) & np.uint64(0xFFFF) for f in range(4)]
+    out = np.stack(parts, axis=2).reshape(-1, 16)                   # element j: word j >> 2, field j & 3
+    return out.astype(np.uint16).reshape(rows, cols)
+
+
 def sr_bf16(x32: np.ndarray, r16: np.ndarray) -> np.ndarray:
     """Stochastic rounding fp32 -> bf16 with the given 16 random bits per element.
 

@@ -113,9 +113,13 @@ def apply_rule(g, W, m, v, opt, hyper, t, seed, w_fmt, state_fmt, row0=0, col0=0
     W_new, m_new, v_new = optimizers.update(opt, hyper, t, g, W64, m64, v64)
     W32 = W_new.astype(np.float32)
     if w_fmt == "bf16":
-        idx = ((np.arange(rows, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(K_full)
-               + np.arange(cols, dtype=np.uint64)[None, :] + np.uint64(col0))
-        W_st = numerics.sr_bf16(W32, numerics.sr_bits(seed, t, idx))
+        if col0 % 16 == 0 and cols % 16 == 0 and K_full % 16 == 0:
+            bits = numerics.sr_bits_block(seed, t, row0, col0, rows, cols, K_full)
+        else:
+            idx = ((np.arange(rows, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(K_full)
+                   + np.arange(cols, dtype=np.uint64)[None, :] + np.uint64(col0))
+            bits = numerics.sr_bits(seed, t, idx)
+        W_st = numerics.sr_bf16(W32, bits)
     else:
         W_st = W32
     return dict(W=W_st, m=_encode_state(m_new, state_fmt, True), v=_encode_state(v_new, state_fmt, False),

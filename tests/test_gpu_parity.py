@@ -54,12 +54,15 @@ def _init_states(opt, state_fmt, rng, N=N, K=K):
     return m, v
 
 
-def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, lo=None, hi=None, tag=""):
-    P.weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W")
+def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, W_old, env=None, tag=""):
+    """env = (lo, hi, moment ranges) from parity.envelope for inputs whose sums are not exact."""
+    lo, hi, mom = env if env is not None else (None, None, {})
+    slack = P.arith_slack(W_old, w_fmt, ref["W64"])
+    P.weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W", slack=slack)
     if pre is not None:
         P.preround_close(pre, ref["W64"] if lo is None else lo, ref["W64"] if hi is None else hi, what=f"{tag} W32")
-    P.state_close(got_m, ref["m"], ref["m64"], state_fmt, f"{tag} m")
-    P.state_close(got_v, ref["v"], ref["v64"], state_fmt, f"{tag} v")
+    P.state_close(got_m, ref["m"], ref["m64"], state_fmt, f"{tag} m", *mom.get("m", (None, None)))
+    P.state_close(got_v, ref["v"], ref["v64"], state_fmt, f"{tag} v", *mom.get("v", (None, None)))
 
 
 EXACT = [(opt, i, w, s) for opt in synth.OPTIMIZERS
@@ -81,7 +84,7 @@ def test_fused_step_exact_inputs_oracle_fed(lib, opt, in_fmt, w_fmt, state_fmt):
         d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
         pre = d.fused(lib, X, dY, opt, h, t, seed, preround=True)
         gW, gm, gv = d.host()
-        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, tag=f"step {t}")
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}")
         W, m, v = ref["W"], ref["m"], ref["v"]
 
 
@@ -96,17 +99,31 @@ def test_fused_free_running_exact_inputs(lib, opt, in_fmt, w_fmt):
     W = synth.random_weight(9, N, K, w_fmt)
     m, v = wgrad.init_states(opt, N, K, "f32")
     d = P.DeviceStep(W, m, v, w_fmt, "f32")
+    carried = 0.0
     for t in range(1, 8):
         _say("exact free-running", opt, in_fmt, w_fmt, "step", t)
         X, dY = synth.integer_case(500 + t, T, N, K, in_fmt)
         ref = wgrad.step(X, dY, W, m, v, opt, h, t, 77, w_fmt, "f32")
         d.fused(lib, X, dY, opt, h, t, 77)
         gW, gm, gv = d.host()
+        # The device carries its own weight.  A difference left by an earlier step (one rounding
+        # of a weight that then moves to a smaller binade can be several ULPs of the new one)
+        # carries over; each step may add one ULP (stochastic-rounding threshold) plus the fp32
+        # rounding of the rule's arithmetic.
+        slack = P.arith_slack(W, w_fmt, ref["W64"])
         if w_fmt == "bf16":
-            dist = P.ulp_distance(gW, ref["W"])
-            assert dist.max() <= 1, f"step {t}: {int((dist > 1).sum())} weights more than 1 ULP away"
+            x, r = numerics.bf16_to_f64(gW), numerics.bf16_to_f64(ref["W"])
+            allowed = carried * (1 + 1e-6) + P.bf16_ulp(ref["W"]) * (1 + 1e-6) + slack
         else:
-            P.weight_close(gW, ref, w_fmt, what=f"step {t} W")
+            x, r = gW.astype(np.float64), ref["W"].astype(np.float64)
+            allowed = carried * (1 + 1e-6) + 1e-6 + 1e-4 * np.abs(r) + slack
+        diff = np.abs(x - r)
+        bad = diff > allowed
+        if bad.any():
+            i = int(np.flatnonzero(bad)[0])
+            raise AssertionError(f"step {t}: {int(bad.sum())} weights off; first got {x.flat[i]:.8e} want "
+                                 f"{r.flat[i]:.8e} (allowed {allowed.flat[i]:.3e}, carried {np.asarray(carried + 0 * x).flat[i]:.3e})")
+        carried = diff
         P.state_close(gm, ref["m"], ref["m64"], "f32", f"step {t} m")
         P.state_close(gv, ref["v"], ref["v64"], "f32", f"step {t} v")
         W, m, v = ref["W"], ref["m"], ref["v"]
@@ -128,11 +145,11 @@ def test_fused_step_gaussian_envelope(lib, opt, in_fmt, w_fmt, state_fmt):
         X, dY = synth.gaussian_case(40 + i, T, N, K, in_fmt)
         ref = wgrad.step(X, dY, W, m, v, opt, h, t, 99, w_fmt, state_fmt)
         tau = P.grad_bound(X, dY)
-        lo, hi = P.envelope(opt, h, t, ref["g"], tau, W, m, v, w_fmt, state_fmt)
+        env = P.envelope(opt, h, t, ref["g"], tau, W, m, v, w_fmt, state_fmt)
         d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
         pre = d.fused(lib, X, dY, opt, h, t, 99, preround=True)
         gW, gm, gv = d.host()
-        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, lo, hi, tag=f"step {t}")
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, env, tag=f"step {t}")
         W, m, v = ref["W"], ref["m"], ref["v"]
 
 
@@ -228,8 +245,8 @@ def test_backward_step_reads_the_old_weight(lib):
     ref = wgrad.step(X, dY, W, m, v, "adamw", h, 1, 3, "bf16", "f32")
     new = wgrad.dgrad_bf16(dY64, numerics.bf16_to_f64(ref["W"]))
     assert P.ulp_distance(got, new).max() > 1          # the reversed order is visibly different
-    P.weight_close(d.host()[0], ref, "bf16", *P.envelope("adamw", h, 1, ref["g"], P.grad_bound(X, dY), W, m, v,
-                                                         "bf16", "f32"))
+    lo, hi, _ = P.envelope("adamw", h, 1, ref["g"], P.grad_bound(X, dY), W, m, v, "bf16", "f32")
+    P.weight_close(d.host()[0], ref, "bf16", lo, hi, slack=P.arith_slack(W, "bf16", ref["W64"]))
 
 
 @pytest.mark.parametrize("Tn", [0, 1, 64, 65])
@@ -243,7 +260,7 @@ def test_edge_token_counts(lib, Tn):
     d = P.DeviceStep(W, m, v, "bf16", "f32")
     pre = d.fused(lib, X, dY, "adamw", h, 1, 4, preround=True)
     gW, gm, gv = d.host()
-    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32")
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W)
     if Tn == 0:  # zero gradient: pure decoupled decay
         np.testing.assert_allclose(pre.cpu().numpy(), numerics.bf16_to_f64(W) * (1 - np.float32(1e-3) * np.float32(0.01)),
                                    rtol=1e-6)
@@ -317,3 +334,83 @@ def test_stochastic_rounding_escapes_the_dead_zone(lib):
     Wg = P.dev_weight(Wb, "bf16")
     lib.wgrad_step(X, dY, Wg, opt="sgd", hyper=h, step=1, seed=5)
     np.testing.assert_array_equal(P.host_weight(Wg, "bf16"), ref["W"])
+
+
+# ----------------------------------------------------------------------------- 256 x 128 DMA path
+# bf16 inputs with N % 256 == 0 and at least 256 tiles of 256 x 128 take the LDS-DMA mainloop.
+N2, K2 = 2048, 4096
+V2 = [("adamw", "bf16", "f32"), ("adamw", "bf16", "int8"), ("lion", "bf16", "f32"), ("nadam", "f32", "f32"),
+      ("radam", "bf16", "f32"), ("sgd_momentum", "bf16", "int8"), ("rmsprop", "f32", "f32")]
+
+
+@pytest.mark.parametrize("opt,w_fmt,state_fmt", V2, ids=["-".join(c) for c in V2])
+def test_v2_exact_inputs_oracle_fed(lib, opt, w_fmt, state_fmt):
+    rng = np.random.default_rng(31)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(33, N2, K2, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng, N2, K2)
+    for i, t in enumerate((1, 6)):
+        _say("v2 exact oracle-fed", opt, w_fmt, state_fmt, "step", t)
+        X, dY = synth.integer_case(300 + i, T, N2, K2, "bf16")
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 5, w_fmt, state_fmt)
+        d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, 5, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}")
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+def test_v2_gaussian_envelope(lib):
+    rng = np.random.default_rng(32)
+    h = synth.default_hyper("adamw")
+    W = synth.random_weight(34, N2, K2, "bf16")
+    m, v = _init_states("adamw", "f32", rng, N2, K2)
+    for i, t in enumerate((1, 3)):
+        _say("v2 gaussian envelope step", t)
+        X, dY = synth.gaussian_case(310 + i, T, N2, K2, "bf16")
+        ref = wgrad.step(X, dY, W, m, v, "adamw", h, t, 6, "bf16", "f32")
+        env = P.envelope("adamw", h, t, ref["g"], P.grad_bound(X, dY), W, m, v, "bf16", "f32")
+        d = P.DeviceStep(W, m, v, "bf16", "f32")
+        pre = d.fused(lib, X, dY, "adamw", h, t, 6, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, env, tag=f"step {t}")
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+@pytest.mark.parametrize("state_fmt", ["f32", "int8"])
+def test_v2_fused_equals_unfused_bitwise(lib, state_fmt):
+    _say("v2 fused vs unfused", state_fmt)
+    rng = np.random.default_rng(35)
+    h = synth.default_hyper("adamw")
+    W = synth.random_weight(36, N2, K2, "bf16")
+    m, v = _init_states("adamw", state_fmt, rng, N2, K2)
+    X, dY = synth.gaussian_case(320, T, N2, K2, "bf16")
+    a = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    b = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    pa = a.fused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    pb, dW = b.unfused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
+    for x, y in zip(a.host(), b.host()):
+        if isinstance(x, tuple):
+            assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+        else:
+            assert np.array_equal(x, y)
+    # the materialised gradient of the unfused path against the oracle
+    ref = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    err = np.abs(dW.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= P.grad_bound(X, dY))
+
+
+@pytest.mark.parametrize("Tn", [0, 1, 63, 64, 65, 129])
+def test_v2_token_counts(lib, Tn):
+    _say("v2 edge T", Tn)
+    h = synth.default_hyper("adamw")
+    X, dY = synth.integer_case(330 + Tn, Tn, N2, K2, "bf16")
+    W = synth.random_weight(37, N2, K2, "bf16")
+    m, v = wgrad.init_states("adamw", N2, K2, "f32")
+    ref = wgrad.step(X, dY, W, m, v, "adamw", h, 1, 8, "bf16", "f32")
+    d = P.DeviceStep(W, m, v, "bf16", "f32")
+    pre = d.fused(lib, X, dY, "adamw", h, 1, 8, preround=True)
+    gW, gm, gv = d.host()
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, tag=f"T={Tn}")

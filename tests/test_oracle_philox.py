@@ -67,3 +67,12 @@ def test_sr_bits_uniform_and_step_independent():
         assert abs(c) < 5.0 / np.sqrt(len(x)), c
     # different seeds give different streams
     assert np.mean(numerics.sr_bits(78, 1, idx[:4096]) == a[:4096]) < 0.01
+
+
+@pytest.mark.parametrize("row0,col0,rows,cols,K", [(0, 0, 3, 48, 64), (5, 16, 7, 32, 128), (1000, 4080, 2, 16, 4096)])
+def test_sr_bits_block_equals_per_element(row0, col0, rows, cols, K):
+    idx = ((np.arange(rows, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(K)
+           + np.arange(cols, dtype=np.uint64)[None, :] + np.uint64(col0))
+    a = numerics.sr_bits(0xABCDEF, 9, idx)
+    b = numerics.sr_bits_block(0xABCDEF, 9, row0, col0, rows, cols, K)
+    np.testing.assert_array_equal(a, b)

@@ -1,0 +1,60 @@
+"""The GPU parity acceptance rules, checked on the CPU: the oracle's own results pass them,
+results with a planted mistake (in a copy of the oracle's output) fail them."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import numerics, wgrad
+from tests import parity as P
+
+
+def _case(opt, w_fmt, state_fmt, gaussian):
+    N, K, T = 128, 256, 96
+    rng = np.random.default_rng(1)
+    W = synth.random_weight(2, N, K, w_fmt)
+    m, v = wgrad.init_states(opt, N, K, state_fmt)
+    X, dY = (synth.gaussian_case if gaussian else synth.integer_case)(3, T, N, K, "bf16")
+    h = synth.default_hyper(opt)
+    ref = wgrad.step(X, dY, W, m, v, opt, h, 2, 11, w_fmt, state_fmt)
+    env = P.envelope(opt, h, 2, ref["g"], P.grad_bound(X, dY), W, m, v, w_fmt, state_fmt) if gaussian else None
+    return W, ref, env, rng
+
+
+@pytest.mark.parametrize("opt", ["adamw", "lion", "sgd_momentum", "rmsprop"])
+@pytest.mark.parametrize("gaussian", [False, True])
+def test_oracle_result_passes_and_planted_errors_fail(opt, gaussian):
+    W, ref, env, rng = _case(opt, "bf16", "f32", gaussian)
+    lo, hi, mom = env if env else (None, None, {})
+    slack = P.arith_slack(W, "bf16", ref["W64"])
+    P.weight_close(ref["W"], ref, "bf16", lo, hi, slack=slack)
+    if ref["m64"] is not None:
+        P.moment_close(ref["m"], ref["m64"], "m", *mom.get("m", (None, None)))
+    # one weight two ULPs off, away from any sign ambiguity
+    bad = ref["W"].copy()
+    i = int(np.argmax(np.abs(numerics.bf16_to_f64(bad))))
+    bad.flat[i] = bad.flat[i] + 2
+    with pytest.raises(AssertionError):
+        P.weight_close(bad, ref, "bf16", lo, hi, slack=slack)
+    if ref["m64"] is not None:
+        mb = ref["m"].copy()
+        j = int(np.argmax(np.abs(mb)))
+        mb.flat[j] *= 1.001
+        with pytest.raises(AssertionError):
+            P.moment_close(mb, ref["m64"], "m", *mom.get("m", (None, None)))
+
+
+def test_int8_state_check():
+    _, ref, _, _ = _case("adamw", "bf16", "int8", False)
+    P.int8_state_close(ref["m"], ref["m"], "m")
+    codes, scales = ref["m"]
+    c2 = codes.copy()
+    c2.flat[5] = np.int8(np.clip(int(c2.flat[5]) + 2, -127, 127)) if abs(int(c2.flat[5])) < 120 else c2.flat[5] - 2
+    with pytest.raises(AssertionError):
+        P.int8_state_close((c2, scales), ref["m"], "m")
+
+
+def test_ulp_helpers():
+    a = numerics.bf16_rne(np.array([1.0, -1.0, 0.02, 1e-30], np.float32))
+    assert np.all(P.ulp_distance(a, a) == 0)
+    assert np.all(P.ulp_distance(a, a + 1) == 1)
+    np.testing.assert_allclose(P.bf16_ulp(a[:3]), [2 ** -7, 2 ** -7, 2 ** -13])
