@@ -86,6 +86,39 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
+def run_one(a, forge, batches, W, m, v, h, seed, T, N, K):
+    """Time one kernel of the headline shape alone (warmup + steps launches)."""
+    import torch
+    dW = torch.empty((N, K), dtype=torch.float32, device="cuda") if a.kernel in ("gemm", "optimizer") else None
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda") if a.kernel == "dgrad" else None
+    if a.kernel == "optimizer":
+        dW.normal_(0, 0.06)
+
+    def once(t):
+        Xd, Dd = batches[t % 2]
+        if a.kernel == "fused":
+            forge.wgrad_step(Xd, Dd, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
+        elif a.kernel == "gemm":
+            forge.wgrad_gemm(Xd, Dd, dW)
+        elif a.kernel == "optimizer":
+            forge.optimizer_step(dW, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
+        else:
+            forge.dgrad(Dd, W, dX)
+    for t in range(1, a.warmup + 1):
+        once(t)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for t in range(a.warmup + 1, a.warmup + a.steps + 1):
+        once(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+    flop = 2.0 * T * N * K
+    print(json.dumps({"kernel": a.kernel, "us_per_launch": round(ms * 1e3, 2),
+                      "tflops": round(flop / (ms * 1e-3) / 1e12, 1) if a.kernel != "optimizer" else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +128,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kernel", choices=["fused", "gemm", "optimizer", "dgrad"], default=None,
+                    help="run only this kernel of the headline shape (for profiler runs); prints its time")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {a.gpus} requested). The fused step shards "
@@ -135,6 +170,10 @@ def main():
     def step(t):
         Xd, Dd = batches[t % 2]
         forge.wgrad_step(Xd, Dd, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
+
+    if a.kernel is not None:
+        run_one(a, forge, batches, W, m, v, h, seed, T, N, K)
+        return
 
     t = 0
     for _ in range(a.warmup):

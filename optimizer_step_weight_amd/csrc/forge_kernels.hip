@@ -75,55 +75,67 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_gemm_kernel(GemmArgs g, flo
   }
 }
 
-// bf16 inputs, 256 x 128 workgroup tiles fed by LDS DMA (forge_mainloop2.h).
+// bf16 inputs, 256 x 128 workgroup tiles fed by LDS DMA (forge_mainloop2.h): 32-token slabs,
+// three in LDS (72 KiB), so two workgroups share a CU and each SIMD runs two waves.
+using Pipe2 = ml2::Pipe<32, 3>;
+constexpr int kOcc2 = 2;
+
 template <int WT, int ST, int OPT>
-__global__ __launch_bounds__(ml2::THREADS, 1) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[ml2::SMEM];
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Pipe2::SMEM];
   const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
   int nb, kb;
   tile_coords(nbN, nbK, nb, kb);
   const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
   ml2::floatx4 acc[8][4];
-  ml2::contract(acc, smem, g, n0, k0);
+  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  ml2::stage_acc(st, acc, 1.0f);
-  __syncthreads();
   const int tid = threadIdx.x;
 #pragma unroll 1
-  for (int s = 0; s < 8; ++s) {
-    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
-    float gr[16];
-    const float* p = st + row * ml2::EPI_LD + kseg * 16;
+  for (int half = 0; half < 2; ++half) {
+    ml2::stage_acc_half(st, acc, 1.0f, half);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < 4; ++s) {
+      const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
+      float gr[16];
+      const float* p = st + row * ml2::EPI_LD + kseg * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+        for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+      }
+      const uint32_t i0 = (uint32_t)(n0 + half * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+      step_segment16<OPT, WT, ST>(gr, i0, e);
     }
-    const uint32_t i0 = (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
-    step_segment16<OPT, WT, ST>(gr, i0, e);
+    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(ml2::THREADS, 1) void wgrad_gemm_kernel2(GemmArgs g, float* dW) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[ml2::SMEM];
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmArgs g, float* dW) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Pipe2::SMEM];
   const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
   int nb, kb;
   tile_coords(nbN, nbK, nb, kb);
   const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
   ml2::floatx4 acc[8][4];
-  ml2::contract(acc, smem, g, n0, k0);
+  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  ml2::stage_acc(st, acc, 1.0f);
-  __syncthreads();
   const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    ml2::stage_acc_half(st, acc, 1.0f, half);
+    __syncthreads();
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
-    const float* p = st + row * ml2::EPI_LD + kseg * 16;
-    float* d = dW + (int64_t)(n0 + row) * g.K + k0 + kseg * 16;
+    for (int s = 0; s < 4; ++s) {
+      const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
+      const float* p = st + row * ml2::EPI_LD + kseg * 16;
+      float* d = dW + (int64_t)(n0 + half * ml2::EPI_ROWS + row) * g.K + k0 + kseg * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
+      for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
+    }
+    __syncthreads();
   }
 }
 

@@ -39,15 +39,24 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define FORGE_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int BM = 256, BN = 128, TK = 64, STAGES = 3, THREADS = 256;
+constexpr int BM = 256, BN = 128, THREADS = 256;
 constexpr int ROW_A = BM * 2;          // bytes per dY token row in LDS (512)
 constexpr int ROW_B = BN * 2;          // bytes per X token row (256)
-constexpr int PANEL_A = TK * ROW_A;    // 32 KiB
-constexpr int PANEL_B = TK * ROW_B;    // 16 KiB
-constexpr int STAGE = PANEL_A + PANEL_B;
-constexpr int SMEM = STAGES * STAGE;   // 147456 bytes
-constexpr int EPI_LD = BN + 4;         // fp32 staging row stride (floats): 256 x 132 x 4 = 135168 bytes
-static_assert(BM * EPI_LD * 4 <= SMEM, "epilogue staging must fit in the stage buffers");
+constexpr int EPI_LD = BN + 4;         // fp32 staging row stride (floats)
+constexpr int EPI_ROWS = 128;          // the epilogue stages the tile in two halves of 128 rows
+
+// Pipeline shape: TK tokens per slab, STAGES slabs in LDS.
+template <int TK_, int STAGES_>
+struct Pipe {
+  static constexpr int TK = TK_, STAGES = STAGES_;
+  static constexpr int PANEL_A = TK * ROW_A, PANEL_B = TK * ROW_B;
+  static constexpr int STAGE = PANEL_A + PANEL_B;
+  static constexpr int SMEM = STAGES * STAGE;
+  static constexpr int DMA_A = PANEL_A / 1024 / 4, DMA_B = PANEL_B / 1024 / 4;  // per wave per slab
+  static constexpr int DMA = DMA_A + DMA_B;
+  static_assert(EPI_ROWS * EPI_LD * 4 <= SMEM, "epilogue staging must fit in the stage buffers");
+  static_assert(TK % 32 == 0 && DMA < 32 && (STAGES == 3 || STAGES == 4), "pipeline shape");
+};
 
 __device__ __forceinline__ int swz(int row) { return 2 * (row & 7); }
 
@@ -80,42 +89,45 @@ __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, const un
 }
 #pragma clang diagnostic pop
 
+template <class P>
 struct Feed {
-  u32x4 rA, rB;                   // dY and X as buffer resources (out-of-range reads give 0)
-  uint32_t offA[8], offB[4];      // per-lane byte offsets of this wave's DMA pieces, token 0
-  uint32_t stepA, stepB;          // bytes per slab (TK rows)
+  u32x4 rA, rB;                           // dY and X as buffer resources (out-of-range reads give 0)
+  uint32_t offA[P::DMA_A], offB[P::DMA_B];  // per-lane byte offsets of this wave's DMA pieces, token 0
+  uint32_t stepA, stepB;                  // bytes per slab (TK rows)
 };
 
-// Per-lane DMA offsets.  Wave w moves dY rows 2 d, 2 d + 1 (d = 8 w + j, j < 8) and X rows
-// 4 x .. 4 x + 3 (x = 4 w + j, j < 4) of every slab.
-__device__ __forceinline__ void make_feed(Feed& f, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+// Per-lane DMA offsets.  A 1 KiB DMA covers 2 dY rows (512 bytes each) or 4 X rows; wave w
+// moves dY rows 2 d, 2 d + 1 (d = DMA_A w + j) and X rows 4 x .. 4 x + 3 (x = DMA_B w + j).
+template <class P>
+__device__ __forceinline__ void make_feed(Feed<P>& f, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                           int n0, int k0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f.rA = make_rsrc(dY, (uint32_t)(T * N * 2));
   f.rB = make_rsrc(X, (uint32_t)(T * K * 2));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int d = 8 * wave + j, r = 2 * d + (lane >> 5), p = lane & 31;
+  for (int j = 0; j < P::DMA_A; ++j) {
+    const int d = P::DMA_A * wave + j, r = 2 * d + (lane >> 5), p = lane & 31;
     const int c = p ^ swz(r);
     f.offA[j] = (uint32_t)(r * N * 2 + n0 * 2 + c * 16);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int x = 4 * wave + j, r = 4 * x + (lane >> 4), p = lane & 15;
+  for (int j = 0; j < P::DMA_B; ++j) {
+    const int x = P::DMA_B * wave + j, r = 4 * x + (lane >> 4), p = lane & 15;
     const int c = p ^ swz(r);
     f.offB[j] = (uint32_t)(r * K * 2 + k0 * 2 + c * 16);
   }
-  f.stepA = (uint32_t)(TK * N * 2);
-  f.stepB = (uint32_t)(TK * K * 2);
+  f.stepA = (uint32_t)(P::TK * N * 2);
+  f.stepB = (uint32_t)(P::TK * K * 2);
 }
 
-__device__ __forceinline__ void issue(const Feed& f, unsigned char* stage, int slab) {
+template <class P>
+__device__ __forceinline__ void issue(const Feed<P>& f, unsigned char* stage, int slab) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(f.rA, f.offA[j] + sa, stage + (8 * wave + j) * 1024);
+  for (int j = 0; j < P::DMA_A; ++j) dma16(f.rA, f.offA[j] + sa, stage + (P::DMA_A * wave + j) * 1024);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(f.rB, f.offB[j] + sb, stage + PANEL_A + (4 * wave + j) * 1024);
+  for (int j = 0; j < P::DMA_B; ++j) dma16(f.rB, f.offB[j] + sb, stage + P::PANEL_A + (P::DMA_B * wave + j) * 1024);
 }
 
 // Byte offset (within a panel) of this lane's transpose-read piece for 16 columns starting at
@@ -133,12 +145,13 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char* panel, int row_bytes
   return __builtin_bit_cast(bf16x8, x);
 }
 
+template <class P>
 __device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
   const unsigned char* pa = stage;
-  const unsigned char* pb = stage + PANEL_A;
+  const unsigned char* pb = stage + P::PANEL_A;
 #pragma unroll
-  for (int kk = 0; kk < TK / 32; ++kk) {
+  for (int kk = 0; kk < P::TK / 32; ++kk) {
     const int r0 = 32 * kk + 4 * q + (i >> 2), r1 = r0 + 16;
     bf16x8 b[4];
 #pragma unroll
@@ -152,7 +165,9 @@ __device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned c
   }
 }
 
-// acc = dW of tile (n0, k0) over all T tokens.  Ends with a barrier (LDS free for reuse).
+// acc = dW of tile (n0, k0) over all T tokens.  STAGES - 1 slabs are in flight ahead of the
+// one being multiplied.  Ends with a barrier (LDS free for reuse).
+template <class P>
 __device__ __forceinline__ void contract(floatx4 (&acc)[8][4], unsigned char* smem, const GemmArgs& g, int n0,
                                          int k0) {
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
@@ -160,31 +175,43 @@ __device__ __forceinline__ void contract(floatx4 (&acc)[8][4], unsigned char* sm
   for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
-  Feed f;
-  make_feed(f, g.dY, g.X, g.T, g.N, g.K, n0, k0);
-  const int nsl = (int)((g.T + TK - 1) / TK);
-  if (nsl > 0) issue(f, smem, 0);
-  if (nsl > 1) issue(f, smem + STAGE, 1);
+  Feed<P> f;
+  make_feed<P>(f, g.dY, g.X, g.T, g.N, g.K, n0, k0);
+  const int nsl = (int)((g.T + P::TK - 1) / P::TK);
+#pragma unroll
+  for (int s = 0; s < P::STAGES - 1; ++s)
+    if (s < nsl) issue<P>(f, smem + s * P::STAGE, s);
   for (int s = 0; s < nsl; ++s) {
-    if (s + 1 < nsl) wait_vm<12>();
-    else wait_vm<0>();
+    // slabs s+1 .. s+STAGES-2 may still be in flight; slab s must have landed
+    const int ahead = min(nsl - 1 - s, P::STAGES - 2);
+    if constexpr (P::STAGES == 3) {
+      if (ahead >= 1) wait_vm<P::DMA>();
+      else wait_vm<0>();
+    } else {
+      if (ahead >= 2) wait_vm<2 * P::DMA>();
+      else if (ahead == 1) wait_vm<P::DMA>();
+      else wait_vm<0>();
+    }
     barrier();
-    if (s + 2 < nsl) issue(f, smem + ((s + 2) % STAGES) * STAGE, s + 2);
-    mma_stage(acc, smem + (s % STAGES) * STAGE, wm, wn);
+    if (s + P::STAGES - 1 < nsl) issue<P>(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
+    mma_stage<P>(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn);
   }
   barrier();
 }
 
-__device__ __forceinline__ void stage_acc(float* st, const floatx4 (&acc)[8][4], float scale) {
+// Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
+// [128][EPI_LD], multiplied by `scale`; the waves holding those rows write them.
+__device__ __forceinline__ void stage_acc_half(float* st, const floatx4 (&acc)[8][4], float scale, int half) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
+  if (wm != half) return;
 #pragma unroll
   for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        st[(wm * 128 + 16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
+        st[(16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
 }
 
 }  // namespace ml2
