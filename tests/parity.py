@@ -242,3 +242,54 @@ def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt):
             lo = np.where(amb, np.minimum(lo, Wd - p["lr"]), lo)
             hi = np.where(amb, np.maximum(hi, Wd + p["lr"]), hi)
     return lo, hi, mom
+
+
+def moment_tol(lo, hi) -> np.ndarray:
+    """The fp32-moment tolerance of moment_close, for the range [lo, hi]."""
+    scale = float(np.max(np.maximum(np.abs(lo), np.abs(hi)))) if np.size(lo) else 0.0
+    return 1e-4 * np.maximum(np.abs(lo), np.abs(hi)) + min(1e-6, 1e-7 * scale)
+
+
+def int8_envelope_close(gpu, lo, hi, signed: bool, what: str):
+    """int8 block-64 moment against the range [lo, hi] (float64) of correct new values.
+
+    The block scale must lie within rel 1e-4 of the block's absmax for some choice of values
+    in the range; each code within one step of the range quantised with the device's own
+    scale (code = rint(x * levels / scale)).  With lo == hi this is the plain rule: codes
+    within 1, scales within rel 1e-4.
+    """
+    codes, scales = gpu
+    rows, cols = codes.shape
+    lv = numerics.levels(signed)
+    tol = moment_tol(lo, hi)
+    lo_, hi_ = lo - tol, hi + tol
+    a_hi = np.maximum(np.abs(lo_), np.abs(hi_))
+    a_lo = np.where((lo_ <= 0) & (hi_ >= 0), 0.0, np.minimum(np.abs(lo_), np.abs(hi_)))
+    s_hi = a_hi.reshape(rows, -1, numerics.BLOCK).max(-1)
+    s_lo = a_lo.reshape(rows, -1, numerics.BLOCK).max(-1)
+    sc = scales.astype(np.float64)
+    bad = (sc < s_lo * (1 - 1e-4)) | (sc > s_hi * (1 + 1e-4))
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} block scales off; first: got {sc.flat[i]:.9e}, "
+                             f"want [{s_lo.flat[i]:.9e}, {s_hi.flat[i]:.9e}]")
+    s = np.repeat(sc, numerics.BLOCK, axis=1)
+    pos = s > 0
+    safe = np.where(pos, s, 1.0)
+    qlo = np.where(pos, lo_ * lv / safe, 0.0)
+    qhi = np.where(pos, hi_ * lv / safe, 0.0)
+    c = codes.astype(np.float64)
+    bad = (c < qlo - 1.5) | (c > qhi + 1.5) | (~pos & (c != 0))
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} int8 codes off; first: got {int(c.flat[i])}, "
+                             f"want [{qlo.flat[i]:.3f}, {qhi.flat[i]:.3f}] +- 1")
+
+
+def grad_bound_rows(X64: np.ndarray, dY64_rows: np.ndarray, g: np.ndarray, fp8: bool) -> np.ndarray:
+    """grad_bound for the rows of W whose dY columns are given (decoded inputs)."""
+    T = X64.shape[0]
+    tau = 2.0 * (T + 1) * U32 * (np.abs(dY64_rows).T @ np.abs(X64))
+    if fp8:
+        tau = tau + 4.0 * U32 * np.abs(g)
+    return tau

@@ -58,3 +58,21 @@ def test_ulp_helpers():
     assert np.all(P.ulp_distance(a, a) == 0)
     assert np.all(P.ulp_distance(a, a + 1) == 1)
     np.testing.assert_allclose(P.bf16_ulp(a[:3]), [2 ** -7, 2 ** -7, 2 ** -13])
+
+
+@pytest.mark.parametrize("gaussian", [False, True])
+def test_int8_envelope_check(gaussian):
+    W, ref, env, _ = _case("adamw", "bf16", "int8", gaussian)
+    mom = env[2] if env else {"m": (ref["m64"], ref["m64"]), "v": (ref["v64"], ref["v64"])}
+    P.int8_envelope_close(ref["m"], *mom["m"], True, "m")
+    P.int8_envelope_close(ref["v"], *mom["v"], False, "v")
+    codes, scales = ref["m"]
+    j = int(np.argmax(np.abs(codes.astype(int))))          # a large code, two steps off
+    c2 = codes.copy()
+    c2.flat[j] = np.int8(int(c2.flat[j]) - 2 * np.sign(int(c2.flat[j])))
+    with pytest.raises(AssertionError):
+        P.int8_envelope_close((c2, scales), *mom["m"], True, "m")
+    s2 = scales.copy()
+    s2.flat[3] *= 1.01                                       # a block scale 1 % off
+    with pytest.raises(AssertionError):
+        P.int8_envelope_close((codes, s2), *mom["m"], True, "m")
