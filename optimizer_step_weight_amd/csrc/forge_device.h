@@ -142,69 +142,96 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
 // ------------------------------------------------------------------ one 16-element segment
-// Applies rule OPT to 16 consecutive elements of one row of W, starting at flat index i0
-// (a multiple of 16).  The weight, moments and scales are read and written here.  For int8
-// moments the 64-element block spans the 4 consecutive lanes lane^1, lane^2 (all four must
-// be active); the lane holding the block's first segment writes the block scale.
-template <int OPT, int WT, int ST>
-__device__ __forceinline__ void step_segment16(const float (&g)[16], uint32_t i0, const EpiArgs& e) {
-  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
-  float w[16], m[16], v[16];
+// The stored state of 16 consecutive elements, as loaded from memory (raw words).
+struct SegIn {
+  u32x4 w[4];   // bf16: w[0..1] used; fp32: w[0..3]
+  u32x4 m[4];   // fp32: m[0..3]; int8: m[0]
+  u32x4 v[4];
+  float ms, vs; // int8 block scales
+};
 
-  // --- loads
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void seg_load(SegIn& x, uint32_t i0, const EpiArgs& e) {
+  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
   if constexpr (WT == FORGE_W_BF16) {
     const uint16_t* wp = static_cast<const uint16_t*>(e.W) + i0;
-    u32x4 a = ld16(wp), b = ld16(wp + 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[2 * q] = __uint_as_float(a[q] << 16);
-      w[2 * q + 1] = __uint_as_float(a[q] & 0xFFFF0000u);
-      w[8 + 2 * q] = __uint_as_float(b[q] << 16);
-      w[8 + 2 * q + 1] = __uint_as_float(b[q] & 0xFFFF0000u);
-    }
+    x.w[0] = ld16(wp);
+    x.w[1] = ld16(wp + 8);
   } else {
     const float* wp = static_cast<const float*>(e.W) + i0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 a = ld16(wp + 4 * q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[4 * q + c] = __uint_as_float(a[c]);
-    }
+    for (int q = 0; q < 4; ++q) x.w[q] = ld16(wp + 4 * q);
   }
   if constexpr (HM) {
     if constexpr (ST == FORGE_S_F32) {
       const float* mp = static_cast<const float*>(e.m) + i0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 a = ld16(mp + 4 * q);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) m[4 * q + c] = __uint_as_float(a[c]);
-      }
+      for (int q = 0; q < 4; ++q) x.m[q] = ld16(mp + 4 * q);
     } else {
-      const u32x4 a = ld16(static_cast<const int8_t*>(e.m) + i0);
-      const float f = e.m_scale[i0 >> 6] * (1.0f / 127.0f);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) m[4 * q + c] = (float)(int8_t)(a[q] >> (8 * c)) * f;
+      x.m[0] = ld16(static_cast<const int8_t*>(e.m) + i0);
+      x.ms = e.m_scale[i0 >> 6];
     }
   }
   if constexpr (HV) {
     if constexpr (ST == FORGE_S_F32) {
       const float* vp = static_cast<const float*>(e.v) + i0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 a = ld16(vp + 4 * q);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[4 * q + c] = __uint_as_float(a[c]);
-      }
+      for (int q = 0; q < 4; ++q) x.v[q] = ld16(vp + 4 * q);
     } else {
-      const u32x4 a = ld16(static_cast<const uint8_t*>(e.v) + i0);
-      const float f = e.v_scale[i0 >> 6] * (1.0f / 255.0f);
+      x.v[0] = ld16(static_cast<const uint8_t*>(e.v) + i0);
+      x.vs = e.v_scale[i0 >> 6];
+    }
+  }
+}
+
+// Applies rule OPT to 16 consecutive elements of one row of W, starting at flat index i0
+// (a multiple of 16).  The weight, moments and scales are read and written here.  For int8
+// moments the 64-element block spans the 4 consecutive lanes lane^1, lane^2 (all four must
+// be active); the lane holding the block's first segment writes the block scale.
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, const SegIn& x, const EpiArgs& e) {
+  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
+  float w[16], m[16], v[16];
+  if constexpr (WT == FORGE_W_BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[2 * q] = __uint_as_float(x.w[0][q] << 16);
+      w[2 * q + 1] = __uint_as_float(x.w[0][q] & 0xFFFF0000u);
+      w[8 + 2 * q] = __uint_as_float(x.w[1][q] << 16);
+      w[8 + 2 * q + 1] = __uint_as_float(x.w[1][q] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[4 * q + c] = __uint_as_float(x.w[q][c]);
+  }
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[4 * q + c] = (float)((a[q] >> (8 * c)) & 0xFFu) * f;
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = __uint_as_float(x.m[q][c]);
+    } else {
+      const float f = x.ms * (1.0f / 127.0f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = (float)(int8_t)(x.m[0][q] >> (8 * c)) * f;
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = __uint_as_float(x.v[q][c]);
+    } else {
+      const float f = x.vs * (1.0f / 255.0f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = (float)((x.v[0][q] >> (8 * c)) & 0xFFu) * f;
     }
   }
 
@@ -328,6 +355,16 @@ __device__ __forceinline__ void step_segment16(const float (&g)[16], uint32_t i0
       if (leader) e.v_scale[i0 >> 6] = amax;
     }
   }
+}
+
+// Applies rule OPT to 16 consecutive elements of one row of W, starting at flat index i0
+// (a multiple of 16): loads the stored state, updates it, writes it back.  For int8 moments
+// the 64-element block spans the 4 consecutive lanes lane^1, lane^2 (all four must be active).
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void step_segment16(const float (&g)[16], uint32_t i0, const EpiArgs& e) {
+  SegIn x;
+  seg_load<OPT, WT, ST>(x, i0, e);
+  seg_apply<OPT, WT, ST>(g, i0, x, e);
 }
 
 }  // namespace forge

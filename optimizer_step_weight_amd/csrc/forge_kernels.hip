@@ -89,25 +89,57 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
   const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+  // Epilogue: the tile's gradient goes through LDS in two 128-row halves; each thread owns 4
+  // segments of 16 elements per half.  The stored state of the next two segments is always in
+  // flight while the current one is updated (the first two loads leave before the staging).
   float* st = reinterpret_cast<float*>(smem);
   const int tid = threadIdx.x;
-#pragma unroll 1
+  auto index_of = [&](int j) {  // flat W index of the thread's j-th segment (j = 4 half + s)
+    const int seg = tid + ml2::THREADS * (j & 3), row = seg >> 3, kseg = seg & 7;
+    return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+  };
+  auto grad = [&](int s, float (&gr)[16]) {
+    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
+    const float* p = st + row * ml2::EPI_LD + kseg * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+    }
+  };
+  // Two segments in flight where the registers allow it: in the first half the other half's
+  // accumulators are still live, so wide states (fp32 weights, int8 moments) keep one.
+  constexpr bool kDeep0 = WT == FORGE_W_BF16 && ST == FORGE_S_F32;
+  SegIn x0, x1;
+  seg_load<OPT, WT, ST>(x0, index_of(0), e);
+  if constexpr (kDeep0) seg_load<OPT, WT, ST>(x1, index_of(1), e);
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
     ml2::stage_acc_half(st, acc, 1.0f, half);
     __syncthreads();
-#pragma unroll 1
-    for (int s = 0; s < 4; ++s) {
-      const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
-      float gr[16];
-      const float* p = st + row * ml2::EPI_LD + kseg * 16;
+    if (half == 0 && !kDeep0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+      for (int s = 0; s < 4; ++s) {
+        float gr[16];
+        grad(s, gr);
+        seg_apply<OPT, WT, ST>(gr, index_of(s), x0, e);
+        if (s < 3) seg_load<OPT, WT, ST>(x0, index_of(s + 1), e);
       }
-      const uint32_t i0 = (uint32_t)(n0 + half * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
-      step_segment16<OPT, WT, ST>(gr, i0, e);
+      seg_load<OPT, WT, ST>(x0, index_of(4), e);
+      seg_load<OPT, WT, ST>(x1, index_of(5), e);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; s += 2) {
+        const int j = 4 * half + s;
+        float gr[16];
+        grad(s, gr);
+        seg_apply<OPT, WT, ST>(gr, index_of(j), x0, e);
+        if (j + 2 < 8) seg_load<OPT, WT, ST>(x0, index_of(j + 2), e);
+        grad(s + 1, gr);
+        seg_apply<OPT, WT, ST>(gr, index_of(j + 1), x1, e);
+        if (j + 3 < 8) seg_load<OPT, WT, ST>(x1, index_of(j + 3), e);
+      }
     }
     __syncthreads();
   }
