@@ -7,11 +7,15 @@ wd 0.01 decoupled), bf16 weight write-back with stochastic rounding.  Inputs are
 and seeded; two input batches alternate so that consecutive steps do not re-read one batch
 from the last-level cache.
 
-Prints one JSON line: throughput in TFLOP/s (2 T N K per step), the roofline of the fused
-kernel, the CPU oracle's rate on a bounded sample of the same step, and side numbers (the
-unfused GEMM + optimizer path, dgrad, peak memory).
+Prints one JSON line: throughput in TFLOP/s (2 T N K per step) over `steps` fused steps run
+back to back after `warmup` untimed ones, the roofline of the fused kernel, the CPU oracle's
+rate on a bounded sample of the same step, and in "extra": per-step p10/p50/p90 warm and cold
+(L2 and last-level cache flushed before each step), the unfused GEMM + optimizer path (same
+protocol) and hipBLASLt's GEMM for the same product as context, dgrad, peak memory, and the
+other workloads (the 7-linear Llama-3.1-8B block with dgrad, the Qwen3-14B block with int8
+moments, the 8-rule sweep with bf16 and fp8 inputs).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps 30] [--warmup 20] [--no-cpu] [--no-extra]
        python bench.py --copy-calibration      (plain copy kernel for HBM counter scaling)
 """
 from __future__ import annotations
@@ -29,6 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused wgrad+AdamW TFLOP/s and % bf16 MFMA peak (8B down_proj, T=4096)"
+# the moments each update rule keeps (which state buffers a call passes)
+RULE_STATES = {"adamw": "mv", "nadam": "mv", "radam": "mv", "lion": "m", "rmsprop": "v", "adagrad": "v",
+               "sgd": "", "sgd_momentum": "m"}
 PMC_FILE = os.path.join(ROOT, "profiles", "fused_adamw_down_proj_T4096_hbm_counters.json")
 
 
@@ -53,8 +60,8 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(rows: int):
-    """The oracle (fp64 two-phase step) on `rows` rows of W with the full T and K."""
+def cpu_baseline(rows: int, steps: int):
+    """The oracle (fp64 two-phase step) on `rows` rows of W with the full T and K, `steps` times."""
     import numpy as np
 
     import synth
@@ -67,12 +74,14 @@ def cpu_baseline(rows: int):
     m, v = wgrad.init_states("adamw", rows, L.K, "f32")
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    wgrad.step(X, dYs, W, m, v, "adamw", w.hyper, 1, synth.sr_seed(2, 0), "bf16", "f32")
+    for t in range(1, steps + 1):
+        r = wgrad.step(X, dYs, W, m, v, "adamw", w.hyper, t, synth.sr_seed(2, 0), "bf16", "f32")
+        W, m, v = r["W"], r["m"], r["v"]
     dt = time.perf_counter() - t0
-    flop = 2.0 * w.T * rows * L.K
+    flop = 2.0 * w.T * rows * L.K * steps
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {L.N} rows of W (full T={w.T}, K={L.K}): fp64 dW by BLAS, fp64 AdamW, "
-                      f"Philox stochastic rounding; {dt:.1f} s"}
+            "sample": f"{steps} steps on {rows} of {L.N} rows of W (full T={w.T}, K={L.K}; one input batch): "
+                      f"fp64 dW by BLAS, fp64 AdamW, Philox stochastic rounding; {dt:.1f} s"}
 
 
 def copy_calibration():
@@ -119,21 +128,184 @@ def run_one(a, forge, batches, W, m, v, h, seed, T, N, K):
                       "tflops": round(flop / (ms * 1e-3) / 1e12, 1) if a.kernel != "optimizer" else None}), flush=True)
 
 
+def pctl(ms_list):
+    """p10 / p50 / p90 of per-step times (ms) in microseconds."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"p10": round(float(np.percentile(a, 10)), 1), "p50": round(float(np.percentile(a, 50)), 1),
+            "p90": round(float(np.percentile(a, 90)), 1)}
+
+
+class Timer:
+    """Per-launch times on the current stream: warm (back to back, one event between launches)
+    and cold (L2 and the last-level cache flushed by a 512 MiB write before each launch,
+    outside the timed region)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.scratch = None
+
+    def warm(self, fn, reps):
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        return ev[0].elapsed_time(ev[reps]) / reps, per
+
+    def cold(self, fn, reps):
+        torch = self.torch
+        if self.scratch is None:
+            self.scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per = []
+        for i in range(reps):
+            self.scratch.fill_(i & 0xFF)
+            torch.cuda.synchronize()
+            e0.record()
+            fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        return per
+
+
+def workload_timings(forge, timer, reps):
+    """The other workloads' steps on device-generated Gaussian inputs of the same shapes and scales:
+    the 7-linear Llama-3.1-8B block (dgrad then the fused step per layer, T = 8192), the Qwen3-14B
+    block with int8 moments (T = 4096), and the 8-rule sweep on W[4096, 4096] (T = 16384) with bf16
+    and fp8 e4m3 inputs."""
+    import torch
+
+    import synth
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+
+    def randn(shape, std, dtype=torch.bfloat16):
+        return (torch.randn(shape, device="cuda", generator=gen) * std).to(dtype)
+
+    def fp8(x):
+        s = (x.float().abs().max() / 448.0).reshape(1)
+        return (x.float() / s).clamp(-448, 448).to(torch.float8_e4m3fn), s
+
+    out = {}
+    # Llama-3.1-8B block: dgrad + fused AdamW step per linear
+    w = synth.WORKLOADS[3]
+    T = w.T
+    layers = []
+    for L in w.layers:
+        layers.append(dict(name=L.name, N=L.N, K=L.K, X=randn((T, L.K), w.x_std), dY=randn((T, L.N), w.dy_std),
+                           W=randn((L.N, L.K), w.w_std), m=torch.zeros((L.N, L.K), device="cuda"),
+                           v=torch.zeros((L.N, L.K), device="cuda"),
+                           dX=torch.empty((T, L.K), dtype=torch.bfloat16, device="cuda")))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
+    per_layer = [[] for _ in layers]
+    block = []
+    for r in range(reps + 2):
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i, d in enumerate(layers):
+            forge.linear_backward_step(d["X"], d["dY"], d["W"], d["dX"], d["m"], d["v"], opt="adamw", hyper=w.hyper,
+                                       step=r + 1, seed=synth.sr_seed(3, i))
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            block.append(ev[0].elapsed_time(ev[-1]))
+            for i in range(len(layers)):
+                per_layer[i].append(ev[i].elapsed_time(ev[i + 1]))
+    flop = sum(4.0 * T * d["N"] * d["K"] for d in layers)
+    b50 = pctl(block)["p50"]
+    out["llama8b_block_T8192_dgrad_plus_step"] = {
+        "block_us": pctl(block), "tflops_wgrad_plus_dgrad": round(flop / (b50 * 1e-6) / 1e12, 1),
+        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)}}
+    del layers
+
+    # Qwen3-14B block, int8 block-64 moments
+    w = synth.WORKLOADS[4]
+    T = w.T
+    layers = []
+    for L in w.layers:
+        layers.append(dict(name=L.name, N=L.N, K=L.K, X=randn((T, L.K), w.x_std), dY=randn((T, L.N), w.dy_std),
+                           W=randn((L.N, L.K), w.w_std),
+                           m=torch.zeros((L.N, L.K), dtype=torch.int8, device="cuda"),
+                           ms=torch.zeros((L.N * L.K // 64,), device="cuda"),
+                           v=torch.zeros((L.N, L.K), dtype=torch.uint8, device="cuda"),
+                           vs=torch.zeros((L.N * L.K // 64,), device="cuda")))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
+    per_layer = [[] for _ in layers]
+    block = []
+    for r in range(reps + 2):
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i, d in enumerate(layers):
+            forge.wgrad_step(d["X"], d["dY"], d["W"], d["m"], d["v"], opt="adamw", hyper=w.hyper, step=r + 1,
+                             seed=synth.sr_seed(4, i), m_scale=d["ms"], v_scale=d["vs"])
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            block.append(ev[0].elapsed_time(ev[-1]))
+            for i in range(len(layers)):
+                per_layer[i].append(ev[i].elapsed_time(ev[i + 1]))
+    flop = sum(2.0 * T * d["N"] * d["K"] for d in layers)
+    b50 = pctl(block)["p50"]
+    out["qwen3_14b_block_T4096_int8_states"] = {
+        "block_us": pctl(block), "tflops": round(flop / (b50 * 1e-6) / 1e12, 1),
+        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)}}
+    del layers
+
+    # optimizer sweep, W[4096, 4096], T = 16384, bf16 and fp8 inputs
+    w = synth.WORKLOADS[5]
+    L = w.layers[0]
+    T = w.T
+    X, dY = randn((T, L.K), w.x_std), randn((T, L.N), w.dy_std)
+    X8, xs = fp8(X)
+    dY8, ds = fp8(dY)
+    sweep = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for fmt in ("bf16", "fp8"):
+        for opt in synth.OPTIMIZERS:
+            W = randn((L.N, L.K), w.w_std)
+            m = torch.zeros((L.N, L.K), device="cuda") if "m" in RULE_STATES[opt] else None
+            v = torch.zeros((L.N, L.K), device="cuda") if "v" in RULE_STATES[opt] else None
+            args = (X, dY, None, None) if fmt == "bf16" else (X8, dY8, xs, ds)
+            times = []
+            for r in range(reps + 4):
+                torch.cuda.synchronize()
+                e0.record()
+                forge.wgrad_step(args[0], args[1], W, m, v, opt=opt, hyper=w.hyper_for(opt), step=r + 1,
+                                 seed=synth.sr_seed(5, synth.OPTIMIZERS.index(opt)), x_scale=args[2], dy_scale=args[3])
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= 4:
+                    times.append(e0.elapsed_time(e1))
+            p50 = pctl(times)["p50"]
+            sweep[f"{opt}-{fmt}"] = {"us_p50": p50, "tflops": round(2.0 * T * L.N * L.K / (p50 * 1e-6) / 1e12, 1)}
+    out["sweep_W4096x4096_T16384"] = sweep
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-extra", action="store_true", help="skip the unfused path, dgrad and the other workloads")
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kernel", choices=["fused", "gemm", "optimizer", "dgrad"], default=None,
                     help="run only this kernel of the headline shape (for profiler runs); prints its time")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {a.gpus} requested). The fused step shards "
-              "by whole weight tiles with no exchange; see DESIGN.md.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (--gpus {a.gpus} requested). Across GPUs the fused step shards "
+              "W by whole 256x128 tiles with the full token count on each GPU (tensor parallelism), which needs "
+              "no exchange on this path, so the per-GPU figure is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -166,94 +338,93 @@ def main():
     m = torch.zeros((N, K), dtype=torch.float32, device="cuda")
     v = torch.zeros((N, K), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    flop = 2.0 * T * N * K
 
-    def step(t):
-        Xd, Dd = batches[t % 2]
-        forge.wgrad_step(Xd, Dd, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
+    def tflops_of(ms):
+        return flop / (ms * 1e-3) / 1e12
 
     if a.kernel is not None:
         run_one(a, forge, batches, W, m, v, h, seed, T, N, K)
         return
 
-    t = 0
-    for _ in range(a.warmup):
-        t += 1
-        step(t)
+    t = [0]
+
+    def step(_i):
+        t[0] += 1
+        Xd, Dd = batches[t[0] % 2]
+        forge.wgrad_step(Xd, Dd, W, m, v, opt="adamw", hyper=h, step=t[0], seed=seed)
+
+    timer = Timer()
+    for i in range(a.warmup):
+        step(i)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(a.steps):
-        t += 1
-        step(t)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / a.steps
+    ms, per_step = timer.warm(step, a.steps)            # the timed region: `steps` fused steps back to back
     fused_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
-    flop = 2.0 * T * N * K
-    tflops = flop / (ms * 1e-3) / 1e12
+    tflops = tflops_of(ms)
     print(f"[bench] fused step {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-
-    extra = {"fused_peak_extra_bytes": int(fused_peak_extra)}
+    extra = {"fused_us_warm": pctl(per_step), "fused_peak_extra_bytes": int(fused_peak_extra)}
     if not a.no_extra:
+        extra["fused_us_cold"] = pctl(timer.cold(step, 10))
         # unfused two-phase baseline: dW GEMM to HBM, then the optimizer kernel
         torch.cuda.reset_peak_memory_stats()
         base_alloc = torch.cuda.memory_allocated()
         dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
 
-        def unfused(t):
-            Xd, Dd = batches[t % 2]
+        def gemm(i):
+            Xd, Dd = batches[i % 2]
             forge.wgrad_gemm(Xd, Dd, dW)
-            forge.optimizer_step(dW, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
-        for _ in range(2):
-            t += 1
-            unfused(t)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        gemm_ms = opt_ms = 0.0
-        for _ in range(a.steps):
-            t += 1
-            Xd, Dd = batches[t % 2]
-            e[0].record()
-            forge.wgrad_gemm(Xd, Dd, dW)
-            e[1].record()
-            forge.optimizer_step(dW, W, m, v, opt="adamw", hyper=h, step=t, seed=seed)
-            e[2].record()
-            torch.cuda.synchronize()
-            gemm_ms += e[0].elapsed_time(e[1])
-            opt_ms += e[1].elapsed_time(e[2])
+
+        def opt_step(_i):
+            t[0] += 1
+            forge.optimizer_step(dW, W, m, v, opt="adamw", hyper=h, step=t[0], seed=seed)
+
+        def unfused(i):
+            gemm(i)
+            opt_step(i)
+        for i in range(3):
+            unfused(i)
+        unf_ms, unf_per = timer.warm(unfused, a.steps)
         unf_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
+        gemm_ms, _ = timer.warm(gemm, a.steps)
+        opt_ms, _ = timer.warm(opt_step, a.steps)
+        unf_cold = timer.cold(unfused, 10)
+        # the vendor GEMM (hipBLASLt through torch) for the same product with fp32 out, as context
+        try:
+            Dt = batches[0][1].t()
+            for _ in range(5):
+                torch.mm(Dt, batches[0][0], out_dtype=torch.float32)
+            vendor_ms, _ = timer.warm(lambda _i: torch.mm(Dt, batches[0][0], out_dtype=torch.float32), a.steps)
+            vendor = round(vendor_ms * 1e3, 1)
+        except (TypeError, RuntimeError):   # a torch without mm(out_dtype=...)
+            vendor = None
         del dW
-        gemm_ms /= a.steps
-        opt_ms /= a.steps
         # dgrad on the same layer (dX = dY W), bf16 out
         dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
-        for _ in range(2):
-            forge.dgrad(batches[0][1], W, dX)
-        ev0.record()
-        for _ in range(a.steps):
-            forge.dgrad(batches[0][1], W, dX)
-        ev1.record()
-        torch.cuda.synchronize()
-        dg_ms = ev0.elapsed_time(ev1) / a.steps
+        dg_ms, _ = timer.warm(lambda _i: forge.dgrad(batches[0][1], W, dX), a.steps)
         del dX
         extra.update({
-            "unfused_ms": round(gemm_ms + opt_ms, 4), "unfused_gemm_ms": round(gemm_ms, 4),
-            "unfused_optimizer_ms": round(opt_ms, 4), "fused_speedup_vs_unfused": round((gemm_ms + opt_ms) / ms, 3),
-            "unfused_peak_extra_bytes": int(unf_peak_extra), "dgrad_ms": round(dg_ms, 4),
-            "dgrad_tflops": round(flop / (dg_ms * 1e-3) / 1e12, 1),
+            "unfused_us": round(unf_ms * 1e3, 1), "unfused_us_warm": pctl(unf_per), "unfused_us_cold": pctl(unf_cold),
+            "unfused_gemm_us": round(gemm_ms * 1e3, 1), "unfused_optimizer_us": round(opt_ms * 1e3, 1),
+            "fused_speedup_vs_unfused": round(unf_ms / ms, 3), "unfused_peak_extra_bytes": int(unf_peak_extra),
+            "vendor_gemm_f32_out_us": vendor, "dgrad_us": round(dg_ms * 1e3, 1),
+            "dgrad_tflops": round(tflops_of(dg_ms), 1),
             "optimizer_kernel_hbm_gbs": round(N * K * (4 + 4 + 8 + 8) / (opt_ms * 1e-3) / 1e9, 1),
         })
-        print(f"[bench] unfused {gemm_ms * 1e3:.1f} + {opt_ms * 1e3:.1f} us; dgrad {dg_ms * 1e3:.1f} us",
-              file=sys.stderr, flush=True)
+        print(f"[bench] unfused {gemm_ms * 1e3:.1f} + {opt_ms * 1e3:.1f} us; dgrad {dg_ms * 1e3:.1f} us; "
+              f"vendor gemm {vendor} us", file=sys.stderr, flush=True)
+        del batches[1]
+        torch.cuda.empty_cache()
+        print("[bench] timing the other workloads", file=sys.stderr, flush=True)
+        extra["workloads"] = workload_timings(forge, timer, 5)
 
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()}
     cpu = None
     if not a.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(a.cpu_rows)
+        cpu = cpu_baseline(a.cpu_rows, a.cpu_steps)
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
