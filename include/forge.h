@@ -138,10 +138,12 @@ forge_status forge_wgrad_step(const forge_tensor* X, const forge_tensor* dY, for
                               const forge_step_opts* opts, void* stream);
 
 /*
- * forge_dgrad -- input gradient dX[T, K] = dY[T, N] . W[N, K] (fp32 accumulation, stored BF16
- * with round-to-nearest-even, or F32).  dY and W BF16 (or both F32).  It reads W as it is when
- * the kernel runs, so enqueue it before forge_wgrad_step on the same stream (Technical Summary
- * section 5: the input gradient must be read before the weight update).
+ * forge_dgrad -- input gradient dX[T, K] = dY[T, N] . W[N, K], accumulated in fp32 and stored
+ * BF16 with round-to-nearest-even.  dY [T, N], W [N, K] and dX [T, K] must all be BF16
+ * (anything else: FORGE_ERR_DTYPE); N and K multiples of 128.  It reads W as it is when the
+ * kernel runs, so enqueue it before forge_wgrad_step on the same stream (Technical Summary
+ * section 5: the input gradient must be read before the weight update).  dX is overwritten and
+ * must not overlap dY or W (FORGE_ERR_ALIAS).
  */
 forge_status forge_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX,
                          void* stream);
