@@ -14,6 +14,8 @@
 // section 5, limitations).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "forge_mainloop.h"
 #include "forge_mainloop2.h"
 
@@ -76,40 +78,52 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_gemm_kernel(GemmArgs g, flo
 }
 
 // bf16 inputs, 256 x 128 workgroup tiles fed by LDS DMA (forge_mainloop2.h): 32-token slabs,
-// three in LDS (72 KiB), so two workgroups share a CU and each SIMD runs two waves.
+// three in LDS (72 KiB), so two workgroups share a CU and each SIMD runs two waves.  The
+// launcher may turn the last k-block columns into 128 x 128 half tiles (four 32-token slabs in
+// LDS) so that the last round of workgroups fills the chip (see plan_split).
 using Pipe2 = ml2::Pipe<32, 3>;
+using Pipe2H = ml2::Pipe<32, 4, 4>;
 constexpr int kOcc2 = 2;
+constexpr int kSmem2 = Pipe2::SMEM;
+static_assert(Pipe2H::SMEM <= kSmem2 && ml2::EPI_BYTES <= kSmem2, "half tiles and the staging share the LDS");
 
+// The thread's 16-element segment s (0..3) of 128 staged rows: row and column in the staging.
+__device__ __forceinline__ void seg_pos(int s, int& row, int& kseg) {
+  const int seg = threadIdx.x + ml2::THREADS * s;
+  row = seg >> 3;
+  kseg = seg & 7;
+}
+
+__device__ __forceinline__ void staged_grad(const float* st, int s, float (&gr)[16]) {
+  int row, kseg;
+  seg_pos(s, row, kseg);
+  const float* p = st + row * ml2::EPI_LD + kseg * 16;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
+  }
+}
+
+// Full 256 x 128 tile.  Epilogue: the gradient goes through LDS in two 128-row halves; each
+// thread owns 4 segments of 16 elements per half.  The stored state of the next two segments
+// is in flight while the current one is updated (the first loads leave before the staging);
+// in the first half the other half's accumulators are still live, so wide states (fp32
+// weights, int8 moments) keep one segment in flight there.
 template <int WT, int ST, int OPT>
-__global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Pipe2::SMEM];
-  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
   int nb, kb;
-  tile_coords(nbN, nbK, nb, kb);
+  tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
   const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
-  // Epilogue: the tile's gradient goes through LDS in two 128-row halves; each thread owns 4
-  // segments of 16 elements per half.  The stored state of the next two segments is always in
-  // flight while the current one is updated (the first two loads leave before the staging).
   float* st = reinterpret_cast<float*>(smem);
-  const int tid = threadIdx.x;
   auto index_of = [&](int j) {  // flat W index of the thread's j-th segment (j = 4 half + s)
-    const int seg = tid + ml2::THREADS * (j & 3), row = seg >> 3, kseg = seg & 7;
+    int row, kseg;
+    seg_pos(j & 3, row, kseg);
     return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
   };
-  auto grad = [&](int s, float (&gr)[16]) {
-    const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
-    const float* p = st + row * ml2::EPI_LD + kseg * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) gr[4 * q + c] = x[c];
-    }
-  };
-  // Two segments in flight where the registers allow it: in the first half the other half's
-  // accumulators are still live, so wide states (fp32 weights, int8 moments) keep one.
   constexpr bool kDeep0 = WT == FORGE_W_BF16 && ST == FORGE_S_F32;
   SegIn x0, x1;
   seg_load<OPT, WT, ST>(x0, index_of(0), e);
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float gr[16];
-        grad(s, gr);
+        staged_grad(st, s, gr);
         seg_apply<OPT, WT, ST>(gr, index_of(s), x0, e);
         if (s < 3) seg_load<OPT, WT, ST>(x0, index_of(s + 1), e);
       }
@@ -133,10 +147,10 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
       for (int s = 0; s < 4; s += 2) {
         const int j = 4 * half + s;
         float gr[16];
-        grad(s, gr);
+        staged_grad(st, s, gr);
         seg_apply<OPT, WT, ST>(gr, index_of(j), x0, e);
         if (j + 2 < 8) seg_load<OPT, WT, ST>(x0, index_of(j + 2), e);
-        grad(s + 1, gr);
+        staged_grad(st, s + 1, gr);
         seg_apply<OPT, WT, ST>(gr, index_of(j + 1), x1, e);
         if (j + 3 < 8) seg_load<OPT, WT, ST>(x1, index_of(j + 3), e);
       }
@@ -145,35 +159,118 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
   }
 }
 
-__global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmArgs g, float* dW) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Pipe2::SMEM];
-  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+// Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once, two
+// segments in flight.
+template <int WT, int ST, int OPT>
+__device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
   int nb, kb;
-  tile_coords(nbN, nbK, nb, kb);
-  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
-  ml2::floatx4 acc[8][4];
-  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+  tile_coords_at(hb, (int)(g.N / ml2::BM_HALF), (int)(g.K / ml2::BN) - g.kb_split, nb, kb);
+  const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_split + kb) * ml2::BN;
+  ml2::floatx4 acc[4][4];
+  ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  const int tid = threadIdx.x;
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    ml2::stage_acc_half(st, acc, 1.0f, half);
-    __syncthreads();
+  auto index_of = [&](int s) {
+    int row, kseg;
+    seg_pos(s, row, kseg);
+    return (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+  };
+  SegIn x0, x1;
+  seg_load<OPT, WT, ST>(x0, index_of(0), e);
+  seg_load<OPT, WT, ST>(x1, index_of(1), e);
+  ml2::stage_acc_all(st, acc, 1.0f);
+  __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int seg = tid + ml2::THREADS * s, row = seg >> 3, kseg = seg & 7;
-      const float* p = st + row * ml2::EPI_LD + kseg * 16;
-      float* d = dW + (int64_t)(n0 + half * ml2::EPI_ROWS + row) * g.K + k0 + kseg * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
-    }
-    __syncthreads();
+  for (int s = 0; s < 4; s += 2) {
+    float gr[16];
+    staged_grad(st, s, gr);
+    seg_apply<OPT, WT, ST>(gr, index_of(s), x0, e);
+    if (s + 2 < 4) seg_load<OPT, WT, ST>(x0, index_of(s + 2), e);
+    staged_grad(st, s + 1, gr);
+    seg_apply<OPT, WT, ST>(gr, index_of(s + 1), x1, e);
+    if (s + 3 < 4) seg_load<OPT, WT, ST>(x1, index_of(s + 3), e);
   }
 }
 
-// The 256 x 128 path needs N % 256 == 0 and enough tiles to give every CU one.
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  const int b = (int)blockIdx.x;
+  if (b < g.nfull) fused_full_tile<WT, ST, OPT>(g, e, smem, b);
+  else fused_half_tile<WT, ST, OPT>(g, e, smem, b - g.nfull);
+}
+
+// dW rows of 128 staged rows, written with 16-byte stores.
+__device__ __forceinline__ void store_staged(const float* st, float* dW, int64_t K, int n0, int k0) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    int row, kseg;
+    seg_pos(s, row, kseg);
+    const float* p = st + row * ml2::EPI_LD + kseg * 16;
+    float* d = dW + (int64_t)(n0 + row) * K + k0 + kseg * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
+  }
+}
+
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmArgs g, float* dW) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  float* st = reinterpret_cast<float*>(smem);
+  const int b = (int)blockIdx.x;
+  int nb, kb;
+  if (b < g.nfull) {
+    tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
+    const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+    ml2::floatx4 acc[8][4];
+    ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      ml2::stage_acc_half(st, acc, 1.0f, half);
+      __syncthreads();
+      store_staged(st, dW, g.K, n0 + half * ml2::EPI_ROWS, k0);
+      __syncthreads();
+    }
+  } else {
+    tile_coords_at(b - g.nfull, (int)(g.N / ml2::BM_HALF), (int)(g.K / ml2::BN) - g.kb_split, nb, kb);
+    const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_split + kb) * ml2::BN;
+    ml2::floatx4 acc[4][4];
+    ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
+    ml2::stage_acc_all(st, acc, 1.0f);
+    __syncthreads();
+    store_staged(st, dW, g.K, n0, k0);
+  }
+}
+
+// Workgroup slots on the current device: two 256 x 128 workgroups per CU.
+static int slots_on_current_device() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+    cached[dev] = 2 * cu;
+  }
+  return cached[dev];
+}
+
+// Tile plan of the 256 x 128 path.  With F full tiles and S workgroup slots, the last round
+// holds F mod S tiles and leaves CUs with one workgroup; turning the last c k-block columns
+// into 128 x 128 half tiles (c = the fewest columns that hold that remainder) ends the launch
+// with a round of half tiles instead.  Returns the grid size.
+static unsigned plan_split(GemmArgs& g) {
+  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+  const int full = nbN * nbK, slots = slots_on_current_device();
+  const int rem = full % slots;
+  const int c = rem == 0 ? 0 : std::min(nbK, (rem + nbN - 1) / nbN);
+  g.kb_split = nbK - c;
+  g.nfull = nbN * g.kb_split;
+  return (unsigned)(g.nfull + 2 * nbN * c);
+}
+
+// The 256 x 128 path needs N % 256 == 0 and at least 128 of its tiles (256 workgroups once the
+// plan turns them into half tiles).
 static bool use_v2(int in_type, const GemmArgs& g) {
-  return in_type == FORGE_IN_BF16 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
+  return in_type == FORGE_IN_BF16 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 128;
 }
 
 // Element-wise rule over a materialised gradient: one thread per 16 consecutive elements.
@@ -339,8 +436,9 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
     else
       fn = s_type == FORGE_S_F32 ? fused2_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused2_for<FORGE_W_F32, FORGE_S_Q8>(opt);
     if (!fn) return (int)hipErrorInvalidValue;
-    const unsigned grid2 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
-    hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, e);
+    GemmArgs g2 = g;
+    const unsigned grid2 = plan_split(g2);
+    hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, e);
     return (int)hipGetLastError();
   }
   if (in_type == FORGE_IN_BF16) fn = fused_for<FORGE_IN_BF16>(w_type, s_type, opt);
@@ -354,8 +452,9 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
 
 int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
   if (use_v2(in_type, g)) {
-    const unsigned grid2 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
-    hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, dW);
+    GemmArgs g2 = g;
+    const unsigned grid2 = plan_split(g2);
+    hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, dW);
     return (int)hipGetLastError();
   }
   const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));

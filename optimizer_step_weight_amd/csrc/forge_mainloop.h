@@ -63,9 +63,8 @@ struct InT<FORGE_IN_FP8> {
 // with its own L2.  Give every XCD a contiguous run of tile ids, and inside a run walk the
 // tiles in groups of 4 n-blocks, so that concurrently running tiles share dY and X panels in
 // their XCD's L2.
-__device__ __forceinline__ void tile_coords(int nbN, int nbK, int& nb, int& kb) {
+__device__ __forceinline__ void tile_coords_at(int b, int nbN, int nbK, int& nb, int& kb) {
   const int nt = nbN * nbK;
-  const int b = blockIdx.x;
   const int per = nt >> 3, rem = nt & 7, x = b & 7, loc = b >> 3;
   const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
   constexpr int G = 4;
@@ -75,6 +74,10 @@ __device__ __forceinline__ void tile_coords(int nbN, int nbK, int& nb, int& kb) 
   const int r = t - gid * group;
   nb = first + r % gsz;
   kb = r / gsz;
+}
+
+__device__ __forceinline__ void tile_coords(int nbN, int nbK, int& nb, int& kb) {
+  tile_coords_at((int)blockIdx.x, nbN, nbK, nb, kb);
 }
 
 // Transpose an 8-row x 16-byte block (rows = tokens) held in registers into per-column token

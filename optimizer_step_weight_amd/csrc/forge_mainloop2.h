@@ -7,12 +7,12 @@
 // Fidelity"), so the token <-> MFMA k-slot assignment only has to be the same for dY and X.
 //
 // Data path (gfx950):
-//  * A slab of 64 tokens of dY[:, n0:n0+256] (32 KiB) and X[:, k0:k0+128] (16 KiB) is
+//  * A slab of TK = 32 tokens of dY[:, n0:n0+256] (16 KiB) and X[:, k0:k0+128] (8 KiB) is
 //    copied to LDS by buffer_load_dwordx4 ... lds: every lane moves 16 bytes and the wave's
 //    64 lanes fill 1 KiB of LDS in lane order.  Rows stay token-major, exactly as in HBM.
 //    Tokens past T read as zero (buffer range check), so a ragged last slab needs no code.
-//  * Three slabs are in flight (3 x 48 KiB of LDS); the copy of slab s+2 is issued while
-//    slab s is multiplied.
+//  * STAGES slabs live in LDS (3 x 24 KiB for full tiles); the copy of slab s + STAGES - 1 is
+//    issued while slab s is multiplied.
 //  * The MFMA operands need 8 tokens of one n (or k) per lane.  ds_read_b64_tr_b16 gives
 //    exactly that from token-major rows: within each group of 16 lanes, lane j receives
 //    element (j % 4) of the 8-byte piece addressed by lane 4 f + j / 4, for f = 0..3.  Lane
@@ -22,8 +22,10 @@
 //    global address each DMA lane fetches; the transpose reads of 8 consecutive token rows
 //    then hit 8 disjoint bank groups.
 //
-// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k), wave tile 128 x 64 = 8 x 4 MFMA
-// 16x16x32 blocks (128 accumulator registers per lane), one workgroup per CU.
+// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k).  Full tiles are 256 x 128 (wave tile
+// 128 x 64 = 8 x 4 MFMA 16x16x32 blocks, 128 accumulator registers per lane); half tiles are
+// 128 x 128 (wave tile 64 x 64) and balance the last round of a launch (see the launcher).
+// Two workgroups per CU.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,23 +41,28 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define FORGE_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int BM = 256, BN = 128, THREADS = 256;
-constexpr int ROW_A = BM * 2;          // bytes per dY token row in LDS (512)
+constexpr int BM = 256, BN = 128, THREADS = 256;   // full tile
+constexpr int BM_HALF = 128;                        // half tile
 constexpr int ROW_B = BN * 2;          // bytes per X token row (256)
 constexpr int EPI_LD = BN + 4;         // fp32 staging row stride (floats)
-constexpr int EPI_ROWS = 128;          // the epilogue stages the tile in two halves of 128 rows
+constexpr int EPI_ROWS = 128;          // the epilogue stages 128 rows of a tile at a time
+constexpr int EPI_BYTES = EPI_ROWS * EPI_LD * 4;
 
-// Pipeline shape: TK tokens per slab, STAGES slabs in LDS.
-template <int TK_, int STAGES_>
+// Pipeline shape: TK tokens per slab, STAGES slabs in LDS, MB 16-row MFMA blocks per wave
+// (tile height 32 MB: 8 -> 256 rows, 4 -> 128 rows).
+template <int TK_, int STAGES_, int MB_ = 8>
 struct Pipe {
-  static constexpr int TK = TK_, STAGES = STAGES_;
+  static constexpr int TK = TK_, STAGES = STAGES_, MB = MB_;
+  static constexpr int TILE_M = 32 * MB;
+  static constexpr int ROW_A = TILE_M * 2;                 // bytes per dY token row in LDS
   static constexpr int PANEL_A = TK * ROW_A, PANEL_B = TK * ROW_B;
   static constexpr int STAGE = PANEL_A + PANEL_B;
   static constexpr int SMEM = STAGES * STAGE;
   static constexpr int DMA_A = PANEL_A / 1024 / 4, DMA_B = PANEL_B / 1024 / 4;  // per wave per slab
   static constexpr int DMA = DMA_A + DMA_B;
-  static_assert(EPI_ROWS * EPI_LD * 4 <= SMEM, "epilogue staging must fit in the stage buffers");
+  static constexpr int CPR_A = ROW_A / 16, RPD_A = 64 / CPR_A;  // 16-byte chunks per row, rows per 1 KiB
   static_assert(TK % 32 == 0 && DMA < 32 && (STAGES == 3 || STAGES == 4), "pipeline shape");
+  static_assert((MB == 8 || MB == 4) && DMA_A >= 1, "tile height");
 };
 
 __device__ __forceinline__ int swz(int row) { return 2 * (row & 7); }
@@ -96,8 +103,9 @@ struct Feed {
   uint32_t stepA, stepB;                  // bytes per slab (TK rows)
 };
 
-// Per-lane DMA offsets.  A 1 KiB DMA covers 2 dY rows (512 bytes each) or 4 X rows; wave w
-// moves dY rows 2 d, 2 d + 1 (d = DMA_A w + j) and X rows 4 x .. 4 x + 3 (x = DMA_B w + j).
+// Per-lane DMA offsets.  A 1 KiB DMA covers RPD_A dY rows (2 of 512 bytes for full tiles, 4 of
+// 256 bytes for half tiles) or 4 X rows; wave w moves dY rows RPD_A d .. (d = DMA_A w + j) and
+// X rows 4 x .. 4 x + 3 (x = DMA_B w + j).
 template <class P>
 __device__ __forceinline__ void make_feed(Feed<P>& f, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                           int n0, int k0) {
@@ -106,7 +114,7 @@ __device__ __forceinline__ void make_feed(Feed<P>& f, const void* dY, const void
   f.rB = make_rsrc(X, (uint32_t)(T * K * 2));
 #pragma unroll
   for (int j = 0; j < P::DMA_A; ++j) {
-    const int d = P::DMA_A * wave + j, r = 2 * d + (lane >> 5), p = lane & 31;
+    const int d = P::DMA_A * wave + j, r = P::RPD_A * d + lane / P::CPR_A, p = lane % P::CPR_A;
     const int c = p ^ swz(r);
     f.offA[j] = (uint32_t)(r * N * 2 + n0 * 2 + c * 16);
   }
@@ -146,7 +154,7 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char* panel, int row_bytes
 }
 
 template <class P>
-__device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn) {
+__device__ __forceinline__ void mma_stage(floatx4 (&acc)[P::MB][4], const unsigned char* stage, int wm, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
   const unsigned char* pa = stage;
   const unsigned char* pb = stage + P::PANEL_A;
@@ -157,8 +165,8 @@ __device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned c
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, ROW_B, r0, r1, wn * 64 + 16 * bj, i);
 #pragma unroll
-    for (int bi = 0; bi < 8; ++bi) {
-      const bf16x8 a = frag(pa, ROW_A, r0, r1, wm * 128 + 16 * bi, i);
+    for (int bi = 0; bi < P::MB; ++bi) {
+      const bf16x8 a = frag(pa, P::ROW_A, r0, r1, wm * 16 * P::MB + 16 * bi, i);
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
     }
@@ -168,11 +176,11 @@ __device__ __forceinline__ void mma_stage(floatx4 (&acc)[8][4], const unsigned c
 // acc = dW of tile (n0, k0) over all T tokens.  STAGES - 1 slabs are in flight ahead of the
 // one being multiplied.  Ends with a barrier (LDS free for reuse).
 template <class P>
-__device__ __forceinline__ void contract(floatx4 (&acc)[8][4], unsigned char* smem, const GemmArgs& g, int n0,
+__device__ __forceinline__ void contract(floatx4 (&acc)[P::MB][4], unsigned char* smem, const GemmArgs& g, int n0,
                                          int k0) {
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi)
+  for (int bi = 0; bi < P::MB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
   Feed<P> f;
@@ -212,6 +220,19 @@ __device__ __forceinline__ void stage_acc_half(float* st, const floatx4 (&acc)[8
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         st[(16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
+}
+
+// Stage all 128 rows of a half tile's accumulators in LDS as fp32 [128][EPI_LD], times `scale`.
+__device__ __forceinline__ void stage_acc_all(float* st, const floatx4 (&acc)[4][4], float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        st[(wm * 64 + 16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
 }
 
 }  // namespace ml2

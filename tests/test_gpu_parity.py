@@ -414,3 +414,31 @@ def test_v2_token_counts(lib, Tn):
     pre = d.fused(lib, X, dY, "adamw", h, 1, 8, preround=True)
     gW, gm, gv = d.host()
     _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, tag=f"T={Tn}")
+
+
+# ----------------------------------------------------------------------------- full + half tiles
+# 4096 x 4224 has 16 x 33 = 528 tiles of 256 x 128: with 512 workgroup slots the launcher keeps
+# 512 full tiles and turns the last k-block column into 32 half tiles of 128 x 128 (the 2048 x
+# 4096 shapes above run as half tiles only).
+N3, K3 = 4096, 4224
+
+
+@pytest.mark.parametrize("opt,state_fmt", [("adamw", "f32"), ("lion", "int8")])
+def test_v2_full_and_half_tiles_exact(lib, opt, state_fmt):
+    _say("v2 full + half tiles exact", opt, state_fmt)
+    rng = np.random.default_rng(41)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(42, N3, K3, "bf16")
+    m, v = _init_states(opt, state_fmt, rng, N3, K3)
+    X, dY = synth.integer_case(340, T, N3, K3, "bf16")
+    ref = wgrad.step(X, dY, W, m, v, opt, h, 3, 12, "bf16", state_fmt)
+    d = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    pre = d.fused(lib, X, dY, opt, h, 3, 12, preround=True)
+    gW, gm, gv = d.host()
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", state_fmt, W, tag="full+half")
+    u = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    pu, dW = u.unfused(lib, X, dY, opt, h, 3, 12, preround=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pre, pu)
+    ref_g = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    np.testing.assert_array_equal(dW.cpu().numpy().astype(np.float64), ref_g)   # exact sums: bitwise
