@@ -290,84 +290,43 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t
 }
 
 // dX[T, K] = dY[T, N] . W[N, K], bf16 in, fp32 accumulate, bf16 (nearest-even) out.
-// Tile 128 tokens x 128 columns; the reduction runs over N in slabs of 64.  The dY slab is
-// already reduction-contiguous and is copied to LDS as is; the W slab is transposed into
-// [k][n] rows like the wgrad panels.
-__global__ __launch_bounds__(kThreads, 2) void dgrad_kernel(const uint16_t* dY, const uint16_t* W, uint16_t* dX,
-                                                            int64_t T, int64_t N, int64_t K) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
-  const int nbK = (int)(K / kBN);
-  const int tb = blockIdx.x / nbK, kb = blockIdx.x % nbK;
-  const int64_t t0 = (int64_t)tb * 128;
-  const int k0 = kb * kBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int op = tid >> 7, lt = tid & 127;
-  // dY role: rows (lt >> 3) + 16 i of the 128-token tile, 16-byte chunk (lt & 7) of the 64-wide slab
-  // W role: rows 8 (lt % 8) + i of the 64-row slab, 16-byte chunk lt / 8 of the 128 columns
-  const int rg = lt & 7, ch = lt >> 3;
-  const int nsl = (int)(N / 64);
-  u32x4 buf[8];
-  auto load = [&](int s) {
-    const int64_t nbase = (int64_t)s * 64;
-    if (op == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = t0 + (lt >> 3) + 16 * i;
-        buf[i] = t < T ? ld16(dY + t * N + nbase + (lt & 7) * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) buf[i] = ld16(W + (nbase + rg * 8 + i) * K + k0 + ch * 8);
-    }
-  };
-  auto store = [&](unsigned char* stage) {
-    if (op == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(stage + ((lt >> 3) + 16 * i) * kLdsRow + (lt & 7) * 16) = buf[i];
-    } else {
-      store_transposed<FORGE_IN_BF16>(stage + kPanel, buf, ch, rg);
-    }
-  };
-  if (nsl > 0) {  // N == 0 leaves dX = 0
-    load(0);
-    store(smem);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsl; ++s) {
-    unsigned char* stage = smem + (s & 1) * kStage;
-    if (s + 1 < nsl) load(s + 1);
-    mma_slab<FORGE_IN_BF16>(acc, stage + wm * 64 * kLdsRow, stage + kPanel + wn * 64 * kLdsRow, lane);
-    if (s + 1 < nsl) store(smem + ((s + 1) & 1) * kStage);
-    __syncthreads();
-  }
+// 256-token x 128-column tiles, the reduction over N in 32-wide slabs fed by LDS DMA
+// (forge_mainloop2.h, dgrad section); two workgroups per CU.
+static_assert(ml2::DgradPipe::SMEM <= kSmem2, "dgrad stages fit the shared buffer size");
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void dgrad_kernel2(const uint16_t* dY, const uint16_t* W,
+                                                                     uint16_t* dX, int64_t T, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  const int nbT = (int)((T + ml2::BM - 1) / ml2::BM), nbK = (int)(K / ml2::BN);
+  int tb, kb;
+  tile_coords_at((int)blockIdx.x, nbT, nbK, tb, kb);
+  const int64_t t0 = (int64_t)tb * ml2::BM;
+  const int k0 = kb * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::dgrad_contract(acc, smem, dY, W, T, N, K, t0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  stage_acc(st, acc, 1.0f);
-  __syncthreads();
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    ml2::stage_acc_half(st, acc, 1.0f, half);
+    __syncthreads();
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
-    const int64_t t = t0 + row;
-    if (t >= T) continue;
-    float gr[16];
-    read_seg16(gr, st, row, kseg);
-    u32x4 a, b;
+    for (int s = 0; s < 4; ++s) {
+      int row, kseg;
+      seg_pos(s, row, kseg);
+      const int64_t t = t0 + half * ml2::EPI_ROWS + row;
+      if (t >= T) continue;
+      float gr[16];
+      staged_grad(st, s, gr);
+      u32x4 a, b;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
-      b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
+      for (int q = 0; q < 4; ++q) {
+        a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
+        b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
+      }
+      uint16_t* d = dX + t * K + k0 + kseg * 16;
+      st16(d, a);
+      st16(d + 8, b);
     }
-    uint16_t* d = dX + t * K + k0 + kseg * 16;
-    st16(d, a);
-    st16(d + 8, b);
+    __syncthreads();
   }
 }
 
@@ -484,8 +443,8 @@ int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n
 }
 
 int launch_dgrad(const void* dY, const void* W, void* dX, int64_t T, int64_t N, int64_t K, void* stream) {
-  const unsigned grid = (unsigned)(((T + 127) / 128) * (K / kBN));
-  hipLaunchKernelGGL(dgrad_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+  const unsigned grid = (unsigned)(((T + ml2::BM - 1) / ml2::BM) * (K / ml2::BN));
+  hipLaunchKernelGGL(dgrad_kernel2, dim3(grid), dim3(ml2::THREADS), 0, (hipStream_t)stream,
                      static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(dX), T,
                      N, K);
   return (int)hipGetLastError();

@@ -235,5 +235,118 @@ __device__ __forceinline__ void stage_acc_all(float* st, const floatx4 (&acc)[4]
         st[(wm * 64 + 16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
 }
 
+
+// ------------------------------------------------------------------ input gradient (dgrad)
+// dX[t, k] = sum_n dY[t, n] W[n, k] for a 256-token x 128-column tile, reduced over n in
+// slabs of TK = 32.  Same data path as the weight gradient with the roles moved:
+//  * the W slab (32 rows of n, 256 bytes each) is the transposed operand, read exactly like
+//    the X panel above (lane (q, j) of an MFMA fragment holds n = 4q..4q+3 and 16+4q..+3 of
+//    column j);
+//  * the dY slab is already reduction-contiguous: 256 token rows of 64 bytes.  A fragment
+//    needs, per token, the same n order, i.e. two 8-byte pieces at bytes 8q and 32 + 8q of
+//    the row, read with ds_read_b64.  The 16-byte chunks of a row are XOR-swizzled with
+//    (row / 4) mod 4, so the 16 rows read by a lane group fall in 16 distinct bank windows.
+struct DgradPipe {
+  static constexpr int TK = 32, STAGES = 3;
+  static constexpr int ROW_D = TK * 2;                   // dY bytes per token row in LDS (64)
+  static constexpr int PANEL_A = 256 * ROW_D;            // 16 KiB
+  static constexpr int PANEL_B = TK * ROW_B;             // 8 KiB
+  static constexpr int STAGE = PANEL_A + PANEL_B, SMEM = STAGES * STAGE;
+  static constexpr int DMA_A = PANEL_A / 1024 / 4, DMA_B = PANEL_B / 1024 / 4, DMA = DMA_A + DMA_B;
+};
+
+__device__ __forceinline__ int swz_d(int row) { return (row >> 2) & 3; }
+
+struct DgradFeed {
+  u32x4 rA, rB;
+  uint32_t offA[DgradPipe::DMA_A], offB[DgradPipe::DMA_B];
+  uint32_t stepA, stepB;
+};
+
+// A 1 KiB DMA covers 16 dY token rows (4 chunks each) or 4 W rows (16 chunks each).
+__device__ __forceinline__ void make_dgrad_feed(DgradFeed& f, const void* dY, const void* W, int64_t T, int64_t N,
+                                                int64_t K, int64_t t0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(dY, (uint32_t)(T * N * 2));
+  f.rB = make_rsrc(W, (uint32_t)(N * K * 2));
+#pragma unroll
+  for (int j = 0; j < DgradPipe::DMA_A; ++j) {
+    const int d = DgradPipe::DMA_A * wave + j, r = 16 * d + (lane >> 2), p = lane & 3;
+    f.offA[j] = (uint32_t)((t0 + r) * N * 2 + 16 * (p ^ swz_d(r)));
+  }
+#pragma unroll
+  for (int j = 0; j < DgradPipe::DMA_B; ++j) {
+    const int x = DgradPipe::DMA_B * wave + j, r = 4 * x + (lane >> 4), p = lane & 15;
+    f.offB[j] = (uint32_t)(r * K * 2 + k0 * 2 + 16 * (p ^ swz(r)));
+  }
+  f.stepA = (uint32_t)(DgradPipe::TK * 2);
+  f.stepB = (uint32_t)(DgradPipe::TK * K * 2);
+}
+
+__device__ __forceinline__ void dgrad_issue(const DgradFeed& f, unsigned char* stage, int slab) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < DgradPipe::DMA_A; ++j)
+    dma16(f.rA, f.offA[j] + sa, stage + (DgradPipe::DMA_A * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < DgradPipe::DMA_B; ++j)
+    dma16(f.rB, f.offB[j] + sb, stage + DgradPipe::PANEL_A + (DgradPipe::DMA_B * wave + j) * 1024);
+}
+
+// dY fragment of token rows row0 .. row0 + 15 for lane group q: n = 4q..4q+3, 16+4q..+3.
+__device__ __forceinline__ bf16x8 dy_frag(const unsigned char* panel, int row, int q) {
+  auto piece = [&](int byte) {
+    const int c = byte >> 4;
+    return *reinterpret_cast<const v4i16*>(panel + row * DgradPipe::ROW_D + 16 * (c ^ swz_d(row)) + (byte & 15));
+  };
+  const v4i16 lo = piece(8 * q), hi = piece(32 + 8 * q);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+__device__ __forceinline__ void dgrad_mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + DgradPipe::PANEL_A;
+  const int r0 = 4 * q + (i >> 2), r1 = r0 + 16;
+  bf16x8 b[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, ROW_B, r0, r1, wn * 64 + 16 * bj, i);
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi) {
+    const bf16x8 a = dy_frag(pa, wm * 128 + 16 * bi + i, q);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
+  }
+}
+
+// acc = dX of tile (t0, k0) over all n.  Same pipelining as contract().
+__device__ __forceinline__ void dgrad_contract(floatx4 (&acc)[8][4], unsigned char* smem, const void* dY, const void* W,
+                                               int64_t T, int64_t N, int64_t K, int64_t t0, int k0) {
+  using P = DgradPipe;
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  DgradFeed f;
+  make_dgrad_feed(f, dY, W, T, N, K, t0, k0);
+  const int nsl = (int)(N / P::TK);
+#pragma unroll
+  for (int s = 0; s < P::STAGES - 1; ++s)
+    if (s < nsl) dgrad_issue(f, smem + s * P::STAGE, s);
+  for (int s = 0; s < nsl; ++s) {
+    const int ahead = min(nsl - 1 - s, P::STAGES - 2);
+    if (ahead >= 1) wait_vm<P::DMA>();
+    else wait_vm<0>();
+    barrier();
+    if (s + P::STAGES - 1 < nsl) dgrad_issue(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
+    dgrad_mma_stage(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn);
+  }
+  barrier();
+}
+
 }  // namespace ml2
 }  // namespace forge

@@ -293,3 +293,17 @@ def grad_bound_rows(X64: np.ndarray, dY64_rows: np.ndarray, g: np.ndarray, fp8: 
     if fp8:
         tau = tau + 4.0 * U32 * np.abs(g)
     return tau
+
+
+def dx_close(got_bits: np.ndarray, dY64: np.ndarray, W64: np.ndarray, what: str = "dX"):
+    """bf16 dX (bits) against the exact dY W: within the bound on any fp32 summation order of the
+    N products, tau = 2 (N + 1) 2^-24 sum_n |dY W|, plus one bf16 ULP of the rounding."""
+    ref = dY64 @ W64
+    tau = 2.0 * (dY64.shape[1] + 1) * U32 * (np.abs(dY64) @ np.abs(W64))
+    got = numerics.bf16_to_f64(got_bits)
+    u = bf16_ulp(numerics.bf16_rne(ref.astype(np.float32))) * (1 + 1e-6)
+    bad = np.abs(got - ref) > tau + u
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements beyond 1 ULP + sum bound; first: "
+                             f"got {got.flat[i]:.8e}, exact {ref.flat[i]:.8e}, bound {tau.flat[i] + u.flat[i]:.3e}")

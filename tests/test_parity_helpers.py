@@ -76,3 +76,17 @@ def test_int8_envelope_check(gaussian):
     s2.flat[3] *= 1.01                                       # a block scale 1 % off
     with pytest.raises(AssertionError):
         P.int8_envelope_close((codes, s2), *mom["m"], True, "m")
+
+
+def test_dx_check():
+    """The oracle's own bf16 dX passes; one element 4 ULP off (at the largest value) fails."""
+    _, dY = synth.gaussian_case(82, 200, 256, 128, "bf16")
+    W = synth.random_weight(83, 256, 384, "bf16")
+    dY64, W64 = wgrad.decode_operand(dY), numerics.bf16_to_f64(W)
+    ref = wgrad.dgrad_bf16(dY64, W64)
+    P.dx_close(ref, dY64, W64)
+    bad = ref.copy()
+    i = int(np.argmax(np.abs(numerics.bf16_to_f64(bad))))
+    bad.flat[i] = bad.flat[i] + 4
+    with pytest.raises(AssertionError):
+        P.dx_close(bad, dY64, W64)
