@@ -18,6 +18,7 @@
 
 #include "forge_mainloop.h"
 #include "forge_mainloop2.h"
+#include "forge_mainloop8.h"
 
 namespace forge {
 
@@ -109,28 +110,26 @@ __device__ __forceinline__ void staged_grad(const float* st, int s, float (&gr)[
 // Full 256 x 128 tile.  Epilogue: the gradient goes through LDS in two 128-row halves; each
 // thread owns 4 segments of 16 elements per half.  The stored state of the next two segments
 // is in flight while the current one is updated (the first loads leave before the staging);
-// in the first half the other half's accumulators are still live, so wide states (fp32
-// weights, int8 moments) keep one segment in flight there.
-template <int WT, int ST, int OPT>
-__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
-  int nb, kb;
-  tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
-  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
-  ml2::floatx4 acc[8][4];
-  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+// in the first half the other half's accumulators are still live, so unless DEEP0 only one
+// segment is in flight there (bf16 weights with fp32 moments on the bf16 path use two).
+// stage(half) writes rows [128 half, 128 half + 128) of the finished tile into the staging.
+// DEEP0: two segments in flight in the first half too (where registers allow it).
+template <int WT, int ST, int OPT, bool DEEP0, class Stage>
+__device__ __forceinline__ void full_tile_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                                   int k0, Stage&& stage) {
   float* st = reinterpret_cast<float*>(smem);
   auto index_of = [&](int j) {  // flat W index of the thread's j-th segment (j = 4 half + s)
     int row, kseg;
     seg_pos(j & 3, row, kseg);
     return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
   };
-  constexpr bool kDeep0 = WT == FORGE_W_BF16 && ST == FORGE_S_F32;
+  constexpr bool kDeep0 = DEEP0;
   SegIn x0, x1;
   seg_load<OPT, WT, ST>(x0, index_of(0), e);
   if constexpr (kDeep0) seg_load<OPT, WT, ST>(x1, index_of(1), e);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    ml2::stage_acc_half(st, acc, 1.0f, half);
+    stage(half);
     __syncthreads();
     if (half == 0 && !kDeep0) {
 #pragma unroll
@@ -157,6 +156,18 @@ __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs
     }
     __syncthreads();
   }
+}
+
+template <int WT, int ST, int OPT>
+__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
+  int nb, kb;
+  tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
+  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+  float* st = reinterpret_cast<float*>(smem);
+  full_tile_epilogue<WT, ST, OPT, WT == FORGE_W_BF16 && ST == FORGE_S_F32>(
+      g, e, smem, n0, k0, [&](int half) { ml2::stage_acc_half(st, acc, 1.0f, half); });
 }
 
 // Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once, two
@@ -240,6 +251,42 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
   }
 }
 
+// fp8 e4m3 inputs, 256 x 128 tiles fed by LDS DMA with 8-bit transpose reads
+// (forge_mainloop8.h); the tensors' scale product multiplies the finished sums at staging.
+static_assert(ml8::SMEM <= kSmem2, "fp8 stages fit the shared buffer size");
+
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  int nb, kb;
+  tile_coords((int)(g.N / ml2::BM), (int)(g.K / ml2::BN), nb, kb);
+  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  ml8::floatx16 acc[4][2];
+  ml8::contract(acc, smem, g, n0, k0);
+  const float scale = g.dy_scale[0] * g.x_scale[0];
+  float* st = reinterpret_cast<float*>(smem);
+  full_tile_epilogue<WT, ST, OPT, false>(g, e, smem, n0, k0,
+                                         [&](int half) { ml8::stage_acc_half(st, acc, scale, half); });
+}
+
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmArgs g, float* dW) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  int nb, kb;
+  tile_coords((int)(g.N / ml2::BM), (int)(g.K / ml2::BN), nb, kb);
+  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  ml8::floatx16 acc[4][2];
+  ml8::contract(acc, smem, g, n0, k0);
+  const float scale = g.dy_scale[0] * g.x_scale[0];
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    ml8::stage_acc_half(st, acc, scale, half);
+    __syncthreads();
+    store_staged(st, dW, g.K, n0 + half * ml2::EPI_ROWS, k0);
+    __syncthreads();
+  }
+}
+
 // Workgroup slots on the current device: two 256 x 128 workgroups per CU.
 static int slots_on_current_device() {
   static int cached[64] = {0};
@@ -271,6 +318,11 @@ static unsigned plan_split(GemmArgs& g) {
 // plan turns them into half tiles).
 static bool use_v2(int in_type, const GemmArgs& g) {
   return in_type == FORGE_IN_BF16 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 128;
+}
+
+// fp8 inputs: the DMA path needs N % 256 == 0 and at least 256 of its tiles.
+static bool use_v8(int in_type, const GemmArgs& g) {
+  return in_type == FORGE_IN_FP8 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
 }
 
 // Element-wise rule over a materialised gradient: one thread per 16 consecutive elements.
@@ -333,6 +385,21 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void dgrad_kernel2(const uint1
 // ------------------------------------------------------------------ dispatch tables
 using FusedFn = void (*)(GemmArgs, EpiArgs);
 using OptFn = void (*)(const float*, int64_t, EpiArgs);
+
+template <int WT, int ST>
+static FusedFn fused8_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return fused_step_kernel8<WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return fused_step_kernel8<WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return fused_step_kernel8<WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return fused_step_kernel8<WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return fused_step_kernel8<WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return fused_step_kernel8<WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return fused_step_kernel8<WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return fused_step_kernel8<WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
 
 template <int WT, int ST>
 static FusedFn fused2_for(int opt) {
@@ -400,6 +467,16 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
     hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, e);
     return (int)hipGetLastError();
   }
+  if (use_v8(in_type, g)) {
+    if (w_type == FORGE_W_BF16)
+      fn = s_type == FORGE_S_F32 ? fused8_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused8_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+    else
+      fn = s_type == FORGE_S_F32 ? fused8_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused8_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+    if (!fn) return (int)hipErrorInvalidValue;
+    const unsigned grid8 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
+    hipLaunchKernelGGL(fn, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, e);
+    return (int)hipGetLastError();
+  }
   if (in_type == FORGE_IN_BF16) fn = fused_for<FORGE_IN_BF16>(w_type, s_type, opt);
   else if (in_type == FORGE_IN_F32) fn = fused_for<FORGE_IN_F32>(w_type, s_type, opt);
   else if (in_type == FORGE_IN_FP8) fn = fused_for<FORGE_IN_FP8>(w_type, s_type, opt);
@@ -414,6 +491,11 @@ int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
     GemmArgs g2 = g;
     const unsigned grid2 = plan_split(g2);
     hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, dW);
+    return (int)hipGetLastError();
+  }
+  if (use_v8(in_type, g)) {
+    const unsigned grid8 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
+    hipLaunchKernelGGL(wgrad_gemm_kernel8, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, dW);
     return (int)hipGetLastError();
   }
   const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));

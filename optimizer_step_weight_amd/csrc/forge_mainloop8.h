@@ -1,0 +1,167 @@
+// forge_mainloop8.h -- token contraction of a 256 x 128 weight tile for fp8 e4m3 inputs with
+// per-tensor scales, fed by global->LDS DMA and 8-bit LDS transpose reads.
+//
+// FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism": the tile's
+// gradient is accumulated over all tokens in fp32 registers; any order of the tokens is a
+// valid summation order (section 2 "Precision and Fidelity").  The fp8 codes are multiplied
+// as they are; the product of the two tensors' scales is applied once, to the finished sum,
+// when the accumulators are staged for the epilogue.
+//
+// Data path (gfx950):
+//  * A slab of 64 tokens of dY[:, n0:n0+256] (16 KiB, 256-byte token rows) and X[:, k0:k0+128]
+//    (8 KiB, 128-byte rows) is copied to LDS by buffer_load_dwordx4 ... lds (16 bytes a lane,
+//    1 KiB a wave, in lane order), three slabs in flight; tokens past T read as zero.
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 (both operands e4m3, unit block scales) consumes one
+//    slab per k-step: lane l holds 32 codes of row / column l % 32, tokens 32 (l / 32) ..
+//    +31.  ds_read_b64_tr_b8 builds them from token-major rows: within a 16-lane group, lane
+//    j receives byte (j % 8) of the 8-byte pieces addressed by lanes 2 f + j / 8 (f = 0..7).
+//    Lane i therefore points at token row (base + i / 2), columns c0 + 8 (i % 2) .. +7, and
+//    lane j gets tokens base .. base + 7 of column c0 + j; four reads (base + 0, 8, 16, 24)
+//    fill a fragment.
+//  * Within one read the 32 lanes of a half wave touch 8 token rows x 32 bytes.  16-byte
+//    chunks are XOR-swizzled so those land in distinct banks: chunk ^ 2 (t mod 8) in the
+//    256-byte dY rows (one row spans all 64 banks), chunk ^ 2 ((t / 2) mod 4) in the
+//    128-byte X rows (two rows share the 64 banks).
+//
+// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k), wave tile 128 x 64 = 4 x 2 MFMA 32 x 32
+// blocks (16 accumulators each, 128 registers per lane), two workgroups per CU.
+#pragma once
+
+#include "forge_mainloop2.h"
+
+namespace forge {
+namespace ml8 {
+
+using ml2::barrier;
+using ml2::dma16;
+using ml2::make_rsrc;
+using ml2::wait_vm;
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+
+constexpr int TK = 64, STAGES = 3;
+constexpr int ROW_A = 256, ROW_B = 128;                 // bytes per token row (fp8 codes)
+constexpr int PANEL_A = TK * ROW_A, PANEL_B = TK * ROW_B;  // 16 KiB, 8 KiB
+constexpr int STAGE = PANEL_A + PANEL_B, SMEM = STAGES * STAGE;
+constexpr int DMA_A = PANEL_A / 1024 / 4, DMA_B = PANEL_B / 1024 / 4, DMA = DMA_A + DMA_B;  // 4 + 2 per wave
+
+__device__ __forceinline__ int swz_a(int row) { return 2 * (row & 7); }
+__device__ __forceinline__ int swz_b(int row) { return 2 * ((row >> 1) & 3); }
+
+struct Feed {
+  u32x4 rA, rB;
+  uint32_t offA[DMA_A], offB[DMA_B];
+  uint32_t stepA, stepB;
+};
+
+// A 1 KiB DMA covers 4 dY rows (16 chunks each) or 8 X rows (8 chunks each).
+__device__ __forceinline__ void make_feed(Feed& f, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+                                          int n0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(dY, (uint32_t)(T * N));
+  f.rB = make_rsrc(X, (uint32_t)(T * K));
+#pragma unroll
+  for (int j = 0; j < DMA_A; ++j) {
+    const int d = DMA_A * wave + j, r = 4 * d + (lane >> 4), p = lane & 15;
+    f.offA[j] = (uint32_t)(r * N + n0 + 16 * (p ^ swz_a(r)));
+  }
+#pragma unroll
+  for (int j = 0; j < DMA_B; ++j) {
+    const int x = DMA_B * wave + j, r = 8 * x + (lane >> 3), p = lane & 7;
+    f.offB[j] = (uint32_t)(r * K + k0 + 16 * (p ^ swz_b(r)));
+  }
+  f.stepA = (uint32_t)(TK * N);
+  f.stepB = (uint32_t)(TK * K);
+}
+
+__device__ __forceinline__ void issue(const Feed& f, unsigned char* stage, int slab) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < DMA_A; ++j) dma16(f.rA, f.offA[j] + sa, stage + (DMA_A * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < DMA_B; ++j) dma16(f.rB, f.offB[j] + sb, stage + PANEL_A + (DMA_B * wave + j) * 1024);
+}
+
+// 32 codes of column c0 + (lane % 32), tokens 32 (lane / 32) .. +31 of the slab: four
+// transpose reads.  Lane i of a 16-lane group addresses token row base + i / 2 and the 8
+// columns c0 + 16 g + 8 (i % 2) .. where g = (lane / 16) % 2 selects the column half.
+template <bool IS_A>
+__device__ __forceinline__ intx8 frag(const unsigned char* panel, int c0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
+  const int col = c0 + 16 * g + 8 * (i & 1);  // multiple of 8: byte offset of the piece
+  intx8 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 32 * h + 8 * r + (i >> 1);
+    const int c = col >> 4;
+    const int off = row * (IS_A ? ROW_A : ROW_B) + 16 * (c ^ (IS_A ? swz_a(row) : swz_b(row))) + (col & 15);
+    const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(FORGE_LDS(v2i32, panel + off));
+    out[2 * r] = x[0];
+    out[2 * r + 1] = x[1];
+  }
+  return out;
+}
+
+__device__ __forceinline__ void mma_stage(floatx16 (&acc)[4][2], const unsigned char* stage, int wm, int wn) {
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + PANEL_A;
+  intx8 b[2];
+#pragma unroll
+  for (int bj = 0; bj < 2; ++bj) b[bj] = frag<false>(pb, wn * 64 + 32 * bj);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    const intx8 a = frag<true>(pa, wm * 128 + 32 * bi);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+      acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[bj], acc[bi][bj], 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// acc = sum over all T tokens of dY8[t, n] X8[t, k] (codes, unscaled) for tile (n0, k0).
+// Ends with a barrier (LDS free for reuse).
+__device__ __forceinline__ void contract(floatx16 (&acc)[4][2], unsigned char* smem, const GemmArgs& g, int n0,
+                                         int k0) {
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+  Feed f;
+  make_feed(f, g.dY, g.X, g.T, g.N, g.K, n0, k0);
+  const int nsl = (int)((g.T + TK - 1) / TK);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nsl) issue(f, smem + s * STAGE, s);
+  for (int s = 0; s < nsl; ++s) {
+    const int ahead = min(nsl - 1 - s, STAGES - 2);
+    if (ahead >= 1) wait_vm<DMA>();
+    else wait_vm<0>();
+    barrier();
+    if (s + STAGES - 1 < nsl) issue(f, smem + ((s + STAGES - 1) % STAGES) * STAGE, s + STAGES - 1);
+    mma_stage(acc, smem + (s % STAGES) * STAGE, wm, wn);
+  }
+  barrier();
+}
+
+// Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
+// [128][EPI_LD], times `scale`.  32 x 32 output layout: register v of lane l holds row
+// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+__device__ __forceinline__ void stage_acc_half(float* st, const floatx16 (&acc)[4][2], float scale, int half) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
+  if (wm != half) return;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        st[(32 * bi + 8 * (v >> 2) + 4 * h + (v & 3)) * ml2::EPI_LD + wn * 64 + 32 * bj + c32] = acc[bi][bj][v] * scale;
+}
+
+}  // namespace ml8
+}  // namespace forge

@@ -54,8 +54,15 @@ def _init_states(opt, state_fmt, rng, N=N, K=K):
     return m, v
 
 
-def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, W_old, env=None, tag=""):
-    """env = (lo, hi, moment ranges) from parity.envelope for inputs whose sums are not exact."""
+def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, W_old, env=None, tag="", lion=None):
+    """env = (lo, hi, moment ranges) from parity.envelope for inputs whose sums are not exact.
+
+    lion = (hyper, step, m_old, v_old) for Lion with exact sums: sign(c) of c = b1 m + (1 - b1) g
+    is still ambiguous where c is within fp32 rounding of 0, so the range with tau = 0 is used.
+    """
+    if env is None and lion is not None:
+        h, t, m_old, v_old = lion
+        env = P.envelope("lion", h, t, ref["g"], np.zeros_like(ref["g"]), W_old, m_old, v_old, w_fmt, state_fmt)
     lo, hi, mom = env if env is not None else (None, None, {})
     slack = P.arith_slack(W_old, w_fmt, ref["W64"])
     P.weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W", slack=slack)
@@ -84,7 +91,8 @@ def test_fused_step_exact_inputs_oracle_fed(lib, opt, in_fmt, w_fmt, state_fmt):
         d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
         pre = d.fused(lib, X, dY, opt, h, t, seed, preround=True)
         gW, gm, gv = d.host()
-        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}")
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
         W, m, v = ref["W"], ref["m"], ref["v"]
 
 
@@ -355,7 +363,8 @@ def test_v2_exact_inputs_oracle_fed(lib, opt, w_fmt, state_fmt):
         d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
         pre = d.fused(lib, X, dY, opt, h, t, 5, preround=True)
         gW, gm, gv = d.host()
-        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}")
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
         W, m, v = ref["W"], ref["m"], ref["v"]
 
 
@@ -434,10 +443,84 @@ def test_v2_full_and_half_tiles_exact(lib, opt, state_fmt):
     d = P.DeviceStep(W, m, v, "bf16", state_fmt)
     pre = d.fused(lib, X, dY, opt, h, 3, 12, preround=True)
     gW, gm, gv = d.host()
-    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", state_fmt, W, tag="full+half")
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", state_fmt, W, tag="full+half",
+             lion=(h, 3, m, v) if opt == "lion" else None)
     u = P.DeviceStep(W, m, v, "bf16", state_fmt)
     pu, dW = u.unfused(lib, X, dY, opt, h, 3, 12, preround=True)
     torch.cuda.synchronize()
     assert torch.equal(pre, pu)
     ref_g = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
     np.testing.assert_array_equal(dW.cpu().numpy().astype(np.float64), ref_g)   # exact sums: bitwise
+
+
+# ----------------------------------------------------------------------------- fp8 DMA path
+# fp8 e4m3 inputs with N % 256 == 0 and at least 256 tiles of 256 x 128 take the 8-bit
+# transpose-read mainloop (64-token slabs; T = 200 leaves a ragged last slab).
+V8 = [("adamw", "bf16", "f32"), ("nadam", "bf16", "int8"), ("lion", "f32", "f32"), ("sgd", "bf16", "f32")]
+
+
+@pytest.mark.parametrize("opt,w_fmt,state_fmt", V8, ids=["-".join(c) for c in V8])
+def test_v8_exact_inputs_oracle_fed(lib, opt, w_fmt, state_fmt):
+    rng = np.random.default_rng(51)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(52, N2, K2, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng, N2, K2)
+    for i, t in enumerate((1, 4)):
+        _say("v8 exact oracle-fed", opt, w_fmt, state_fmt, "step", t)
+        X, dY = synth.integer_case(350 + i, T, N2, K2, "fp8")
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 7, w_fmt, state_fmt)
+        d = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, 7, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, state_fmt, W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+def test_v8_gaussian_envelope(lib):
+    rng = np.random.default_rng(53)
+    h = synth.default_hyper("adamw")
+    W = synth.random_weight(54, N2, K2, "bf16")
+    m, v = _init_states("adamw", "f32", rng, N2, K2)
+    _say("v8 gaussian envelope")
+    X, dY = synth.gaussian_case(360, T, N2, K2, "fp8")
+    ref = wgrad.step(X, dY, W, m, v, "adamw", h, 2, 8, "bf16", "f32")
+    env = P.envelope("adamw", h, 2, ref["g"], P.grad_bound(X, dY), W, m, v, "bf16", "f32")
+    d = P.DeviceStep(W, m, v, "bf16", "f32")
+    pre = d.fused(lib, X, dY, "adamw", h, 2, 8, preround=True)
+    gW, gm, gv = d.host()
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, env, tag="fp8 gaussian")
+
+
+def test_v8_fused_equals_unfused_bitwise(lib):
+    _say("v8 fused vs unfused")
+    rng = np.random.default_rng(55)
+    h = synth.default_hyper("adamw")
+    W = synth.random_weight(56, N2, K2, "bf16")
+    m, v = _init_states("adamw", "f32", rng, N2, K2)
+    X, dY = synth.gaussian_case(361, T, N2, K2, "fp8")
+    a = P.DeviceStep(W, m, v, "bf16", "f32")
+    b = P.DeviceStep(W, m, v, "bf16", "f32")
+    pa = a.fused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    pb, dW = b.unfused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
+    for x, y in zip(a.host(), b.host()):
+        assert np.array_equal(x, y)
+    ref = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    err = np.abs(dW.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= P.grad_bound(X, dY))
+
+
+@pytest.mark.parametrize("Tn", [0, 1, 63, 64, 65, 129])
+def test_v8_token_counts(lib, Tn):
+    _say("v8 edge T", Tn)
+    h = synth.default_hyper("adamw")
+    X, dY = synth.integer_case(370 + Tn, Tn, N2, K2, "fp8")
+    W = synth.random_weight(57, N2, K2, "bf16")
+    m, v = wgrad.init_states("adamw", N2, K2, "f32")
+    ref = wgrad.step(X, dY, W, m, v, "adamw", h, 1, 8, "bf16", "f32")
+    d = P.DeviceStep(W, m, v, "bf16", "f32")
+    pre = d.fused(lib, X, dY, "adamw", h, 1, 8, preround=True)
+    gW, gm, gv = d.host()
+    _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, tag=f"fp8 T={Tn}")

@@ -139,7 +139,7 @@ def _check_dgrad(dX, dY64, W_old64, tag):
     P.dx_close(got, dY64[tr], W_old64, f"{tag} dX")
 
 
-def run_layer(lib, w, li, opt, in_fmt, steps, seed, drift_frac=2e-3):
+def run_layer(lib, w, li, opt, in_fmt, steps, seed, drift_frac=1e-2):
     """Run `steps` full-size steps of layer `li` of workload `w`; compare sampled rows."""
     L = w.layers[li]
     N, K, T = L.N, L.K, w.T
@@ -193,8 +193,10 @@ def run_layer(lib, w, li, opt, in_fmt, steps, seed, drift_frac=2e-3):
                   f"{'ULP' if w.w_fmt == 'bf16' else 'rel'}, W beyond 1 ULP {max(r[3] for r in last):.2e}, "
                   f"moments {max(r[4] for r in last):.2e}", flush=True)
     # Free-running rows are not held to the parity bar: where |g| is within the summation error
-    # of zero, sign-driven updates (Adam's first steps, Lion) legitimately go either way and the
-    # two trajectories then differ by about 2 lr.  Such elements must stay rare.
+    # of zero, sign-driven updates (Adam's and RMSprop's first steps, Lion) legitimately go
+    # either way and the two trajectories then differ by about 2 lr; such elements accumulate
+    # over the steps (0.26 % after 8 steps at most, RMSprop with fp8 inputs).  A systematic
+    # error (a wrong rule, rounding or index) moves most elements, so 1 % bounds the report.
     for t, b, wmax, wfrac, mom in report:
         assert wfrac <= drift_frac, f"free rows {b}: {wfrac:.2e} of W beyond tolerance after step {t}"
         if w.state_fmt == "int8":
