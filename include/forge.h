@@ -140,7 +140,8 @@ forge_status forge_wgrad_step(const forge_tensor* X, const forge_tensor* dY, for
 /*
  * forge_dgrad -- input gradient dX[T, K] = dY[T, N] . W[N, K], accumulated in fp32 and stored
  * BF16 with round-to-nearest-even.  dY [T, N], W [N, K] and dX [T, K] must all be BF16
- * (anything else: FORGE_ERR_DTYPE); N and K multiples of 128.  It reads W as it is when the
+ * (anything else: FORGE_ERR_DTYPE); N and K multiples of 128; (T + 256) N and N K each below
+ * 2^31 elements (32-bit byte offsets; else FORGE_ERR_SHAPE).  It reads W as it is when the
  * kernel runs, so enqueue it before forge_wgrad_step on the same stream (Technical Summary
  * section 5: the input gradient must be read before the weight update).  dX is overwritten and
  * must not overlap dY or W (FORGE_ERR_ALIAS).

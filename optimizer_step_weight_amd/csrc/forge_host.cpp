@@ -351,6 +351,9 @@ forge_status forge_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_te
   if (W->rows != N) return fail(FORGE_ERR_SHAPE, "W has %lld rows, dY has %lld columns", (long long)W->rows, (long long)N);
   if (dX->rows != T || dX->cols != K) return fail(FORGE_ERR_SHAPE, "dX must be [T, K]");
   if (N % 128 || K % 128) return fail(FORGE_ERR_SHAPE, "N and K must be multiples of 128");
+  // the kernel addresses dY (padded to whole 256-token tiles) and W with 32-bit byte offsets
+  if ((T + 256) * N * 2 >= (int64_t(1) << 32) || N * K * 2 >= (int64_t(1) << 32))
+    return fail(FORGE_ERR_SHAPE, "dY (plus one tile of tokens) and W must each stay below 4 GiB");
   const Range o = range_of(dX->data, bytes_of(dX), "dX");
   if (overlap(o, range_of(dY->data, bytes_of(dY), "dY")) || overlap(o, range_of(W->data, bytes_of(W), "W")))
     return fail(FORGE_ERR_ALIAS, "dX overlaps an input");

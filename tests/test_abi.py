@@ -101,6 +101,11 @@ def test_dgrad_and_unfused_validation(forge):
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 256, f.BF16, 2 * GB)), None) == 2
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 384, f.F32, 2 * GB)), None) == 3
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 384, f.BF16, 0)), None) == 5
+    # 32-bit offsets: W of 2^31 elements, or dY that reaches 2^31 elements with one tile of tokens
+    assert L.forge_dgrad(r(_t(f, 100, 131072, f.BF16)), r(_t(f, 131072, 16384, f.BF16, GB)),
+                         r(_t(f, 100, 16384, f.BF16, 2 * GB)), None) == 2
+    assert L.forge_dgrad(r(_t(f, 131072 - 256, 16384, f.BF16)), r(_t(f, 16384, 128, f.BF16, 8 * GB)),
+                         r(_t(f, 131072 - 256, 128, f.BF16, 9 * GB)), None) == 2
     X = _t(f, 100, 384, f.BF16, 3 * GB)
     assert L.forge_wgrad_gemm(r(X), r(dY), r(_t(f, 256, 384, f.BF16, 4 * GB)), None) == 3
     assert L.forge_wgrad_gemm(r(X), r(dY), r(_t(f, 256, 256, f.F32, 4 * GB)), None) == 2
