@@ -73,6 +73,11 @@ def cpu_baseline(rows: int, steps: int):
     dYs = synth.Operand("bf16", np.ascontiguousarray(dY.data[:, :rows]))
     m, v = wgrad.init_states("adamw", rows, L.K, "f32")
     cores = len(os.sched_getaffinity(0))
+    try:
+        blas = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+        blas = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except (TypeError, AttributeError):
+        blas = "unknown"
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         r = wgrad.step(X, dYs, W, m, v, "adamw", w.hyper, t, synth.sr_seed(2, 0), "bf16", "f32")
@@ -81,7 +86,7 @@ def cpu_baseline(rows: int, steps: int):
     flop = 2.0 * w.T * rows * L.K * steps
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{steps} steps on {rows} of {L.N} rows of W (full T={w.T}, K={L.K}; one input batch): "
-                      f"fp64 dW by BLAS, fp64 AdamW, Philox stochastic rounding; {dt:.1f} s"}
+                      f"fp64 dW by BLAS ({blas}), fp64 AdamW, Philox stochastic rounding; {dt:.1f} s"}
 
 
 def copy_calibration():
