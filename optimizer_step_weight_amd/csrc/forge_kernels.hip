@@ -1,17 +1,23 @@
 // forge_kernels.hip -- kernels and launchers of the fused and the unfused paths.
 //
 // Fused (FORGE explainer, gist.science, Technical Summary section 2 "Core Mechanism"): one
-// workgroup per 128 x 128 tile of W contracts dY and X over all tokens into fp32
-// accumulators, then applies the optimizer to the tile and writes back only W and its
-// moments.  The gradient tile lives in registers and, for the re-layout to 16 consecutive
-// columns per thread, in the workgroup's LDS; it never reaches HBM.
+// workgroup per tile of W contracts dY and X over all tokens into fp32 accumulators, then
+// applies the optimizer to the tile and writes back only W and its moments.  The gradient
+// tile lives in registers and, for the re-layout to 16 consecutive columns per thread, in the
+// workgroup's LDS; it never reaches HBM.  Three contraction paths, chosen per call:
+//   * bf16 inputs: 256 x 128 tiles (two of the method's 128 x 128 tiles) fed by LDS DMA,
+//     with 128 x 128 half tiles balancing the last round of the launch (forge_mainloop2.h);
+//   * fp8 e4m3 inputs: the same tiles with 8-bit transpose reads (forge_mainloop8.h);
+//   * fp32 inputs and layers with too few tiles: 128 x 128 tiles staged through registers
+//     (forge_mainloop.h).
+// The element-wise update of a 16-element segment (forge_device.h) is shared by all of them.
 //
 // Unfused baseline (Technical Summary section 1 "The Problem"): the same contraction writes
 // the fp32 gradient to HBM, and a separate element-wise kernel reads it back and applies the
 // same update code.
 //
-// dgrad: dX = dY W, run before the step so that it sees the old weight (Technical Summary
-// section 5, limitations).
+// dgrad: dX = dY W on the LDS-DMA path, run before the step so that it sees the old weight
+// (Technical Summary section 5, limitations).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
