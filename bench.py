@@ -302,7 +302,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the unfused path, dgrad and the other workloads")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--cpu-steps", type=int, default=6)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kernel", choices=["fused", "gemm", "optimizer", "dgrad"], default=None,
                     help="run only this kernel of the headline shape (for profiler runs); prints its time")

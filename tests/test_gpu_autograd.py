@@ -88,7 +88,7 @@ def _train(make_layers, steps, seed, lr):
         loss.backward()
         if opt:
             opt.step()
-        losses.append(float(loss))
+        losses.append(loss.detach().item())
     return np.array(losses)
 
 
