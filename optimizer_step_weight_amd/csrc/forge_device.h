@@ -357,6 +357,208 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
   }
 }
 
+// ------------------------------------------------------------------ one 4-element unit
+// Lane-contiguous layout of the epilogue: consecutive lanes hold consecutive 4-element units
+// of a row, so every load and store of a wave covers contiguous memory (streaming reads and
+// writes of the same bytes run ~18 % faster this way than with 64-byte-strided lanes).  The 16
+// elements of one stochastic-rounding counter are then the units of the 4 lanes of a quad, and
+// a 64-element int8 block the units of 16 consecutive lanes.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 x) { *reinterpret_cast<u32x2*>(p) = x; }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ void st4(void* p, uint32_t x) { *reinterpret_cast<uint32_t*>(p) = x; }
+
+struct UnitIn {
+  u32x4 w;       // bf16: w.x, w.y hold the 4 weights; fp32: all four
+  u32x4 m, v;    // fp32 moments; int8: .x holds the 4 codes
+  float ms, vs;  // int8 block scales
+};
+
+// Loads the stored state of the unit at flat index i0 (a multiple of 4).
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void unit_load(UnitIn& x, uint32_t i0, const EpiArgs& e) {
+  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
+  if constexpr (WT == FORGE_W_BF16) {
+    const u32x2 a = ld8(static_cast<const uint16_t*>(e.W) + i0);
+    x.w.x = a.x;
+    x.w.y = a.y;
+  } else {
+    x.w = ld16(static_cast<const float*>(e.W) + i0);
+  }
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
+      x.m = ld16(static_cast<const float*>(e.m) + i0);
+    } else {
+      x.m.x = ld4(static_cast<const int8_t*>(e.m) + i0);
+      x.ms = e.m_scale[i0 >> 6];
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+      x.v = ld16(static_cast<const float*>(e.v) + i0);
+    } else {
+      x.v.x = ld4(static_cast<const uint8_t*>(e.v) + i0);
+      x.vs = e.v_scale[i0 >> 6];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t pick4(const U64x4& o, int j) {
+  const uint64_t a = j == 1 ? o.w[1] : o.w[0];
+  const uint64_t b = j == 3 ? o.w[3] : o.w[2];
+  return j >= 2 ? b : a;
+}
+
+// Stochastic-rounding words of 4 rounds of units.  In round r this lane's unit starts at flat
+// index i[r]; the quad's 4 lanes hold the 16 elements of counter i[r] >> 4 (lane u the unit u,
+// which takes word u of the Philox block).  Lane u computes the block of round u, then the quad
+// exchanges words so that out[r] is word u of round r's block.  All 4 lanes of every quad must
+// be active.
+__device__ __forceinline__ void sr_words4(const uint32_t (&i)[4], const EpiArgs& e, uint64_t (&out)[4]) {
+  const int lane = (int)(threadIdx.x & 63), u = lane & 3, qb = lane & ~3;
+  const uint32_t mine = u == 0 ? i[0] : u == 1 ? i[1] : u == 2 ? i[2] : i[3];
+  const U64x4 o = philox4x64_10((uint64_t)(mine >> 4), e.step, 0ull, 0ull, e.seed, 0ull);
+  // step k: lane s offers word (s - k) mod 4 of its block; lane u reads lane (u + k) mod 4 and
+  // so receives word u of round (u + k) mod 4
+  auto step = [&](int k) {
+    const uint64_t offer = pick4(o, (u - k) & 3);
+    const int src = qb + ((u + k) & 3);
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)offer, src);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(offer >> 32), src);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  };
+  const uint64_t g0 = step(0), g1 = step(1), g2 = step(2), g3 = step(3);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = (r - u) & 3;  // the step that delivered round r
+    out[r] = k == 0 ? g0 : k == 1 ? g1 : k == 2 ? g2 : g3;
+  }
+}
+
+// Applies rule OPT to the 4 elements of the unit at flat index i0 (a multiple of 4) and writes
+// the weight and moments back.  srw: this unit's stochastic-rounding word (field c of it rounds
+// element i0 + c).  For int8 moments the 16 lanes lane ^ 1, 2, 4, 8 hold the 64-element block
+// and must all be active; the lane of its first unit writes the block scale.
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, const UnitIn& x, uint64_t srw,
+                                           const EpiArgs& e) {
+  constexpr bool HM = RuleStates<OPT>::m, HV = RuleStates<OPT>::v;
+  float w[4], m[4], v[4];
+  if constexpr (WT == FORGE_W_BF16) {
+    w[0] = __uint_as_float(x.w.x << 16);
+    w[1] = __uint_as_float(x.w.x & 0xFFFF0000u);
+    w[2] = __uint_as_float(x.w.y << 16);
+    w[3] = __uint_as_float(x.w.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = __uint_as_float(x.w[c]);
+  }
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m[c] = __uint_as_float(x.m[c]);
+    } else {
+      const float f = x.ms * (1.0f / 127.0f);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m[c] = (float)(int8_t)(x.m.x >> (8 * c)) * f;
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(x.v[c]);
+    } else {
+      const float f = x.vs * (1.0f / 255.0f);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = (float)((x.v.x >> (8 * c)) & 0xFFu) * f;
+    }
+  }
+
+  float wn[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float mc = HM ? m[c] : 0.0f, vc = HV ? v[c] : 0.0f;
+    wn[c] = rule<OPT>(g[c], w[c], mc, vc, e.s);
+    m[c] = mc;
+    v[c] = vc;
+  }
+
+  if (e.w_pre) {
+    u32x4 a;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(wn[c]);
+    st16(e.w_pre + i0, a);
+  }
+
+  if constexpr (WT == FORGE_W_BF16) {
+    uint32_t r[4];
+    if (e.sr) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r[c] = f32_to_bf16_sr(wn[c], (uint32_t)(srw >> (16 * c)) & 0xFFFFu);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r[c] = f32_to_bf16_rne(wn[c]);
+    }
+    st8(static_cast<uint16_t*>(e.W) + i0, u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)});
+  } else {
+    u32x4 a;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(wn[c]);
+    st16(static_cast<float*>(e.W) + i0, a);
+  }
+
+  const bool leader = ((i0 >> 2) & 15u) == 0u;
+  if constexpr (HM) {
+    if constexpr (ST == FORGE_S_F32) {
+      u32x4 a;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(m[c]);
+      st16(static_cast<float*>(e.m) + i0, a);
+    } else {
+      float amax = fmaxf(fmaxf(fabsf(m[0]), fabsf(m[1])), fmaxf(fabsf(m[2]), fabsf(m[3])));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      amax = fmaxf(amax, __shfl_xor(amax, 8));
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float qv = __builtin_rintf(m[c] * inv);
+        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+        word |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * c);
+      }
+      st4(static_cast<int8_t*>(e.m) + i0, word);
+      if (leader) e.m_scale[i0 >> 6] = amax;
+    }
+  }
+  if constexpr (HV) {
+    if constexpr (ST == FORGE_S_F32) {
+      u32x4 a;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[c]);
+      st16(static_cast<float*>(e.v) + i0, a);
+    } else {
+      float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      amax = fmaxf(amax, __shfl_xor(amax, 8));
+      const float inv = amax > 0.0f ? 255.0f / amax : 0.0f;
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float qv = __builtin_rintf(v[c] * inv);
+        qv = fminf(fmaxf(qv, 0.0f), 255.0f);
+        word |= ((uint32_t)qv & 0xFFu) << (8 * c);
+      }
+      st4(static_cast<uint8_t*>(e.v) + i0, word);
+      if (leader) e.v_scale[i0 >> 6] = amax;
+    }
+  }
+}
+
 // Applies rule OPT to 16 consecutive elements of one row of W, starting at flat index i0
 // (a multiple of 16): loads the stored state, updates it, writes it back.  For int8 moments
 // the 64-element block spans the 4 consecutive lanes lane^1, lane^2 (all four must be active).

@@ -118,52 +118,83 @@ __device__ __forceinline__ void staged_grad(const float* st, int s, float (&gr)[
 // is in flight while the current one is updated (the first loads leave before the staging);
 // in the first half the other half's accumulators are still live, so unless DEEP0 only one
 // segment is in flight there (bf16 weights with fp32 moments on the bf16 path use two).
-// stage(half) writes rows [128 half, 128 half + 128) of the finished tile into the staging.
-// DEEP0: two segments in flight in the first half too (where registers allow it).
-template <int WT, int ST, int OPT, bool DEEP0, class Stage>
-__device__ __forceinline__ void full_tile_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
-                                                   int k0, Stage&& stage) {
+// ---- epilogue in the lane-contiguous unit layout (forge_device.h, "one 4-element unit")
+// 128 staged rows are 16 rounds of 8 rows: in round rho this thread's unit is row
+// 8 rho + 2 wave + lane / 32, columns 4 (lane % 32) .. +3, so a wave touches two contiguous row
+// segments per access.  Batches of 4 rounds share one Philox block per quad.
+__device__ __forceinline__ int unit_row(int rho) {
+  return 8 * rho + 2 * (int)(threadIdx.x >> 6) + (int)((threadIdx.x & 63) >> 5);
+}
+__device__ __forceinline__ int unit_col() { return 4 * (int)(threadIdx.x & 31); }
+
+// rows0: the tile row of staged row 0 (n0 + 128 half)
+__device__ __forceinline__ uint32_t unit_index(const GemmArgs& g, int rows0, int k0, int rho) {
+  return (uint32_t)(rows0 + unit_row(rho)) * (uint32_t)g.K + (uint32_t)(k0 + unit_col());
+}
+
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void unit_batch_load(UnitIn (&x)[4], const GemmArgs& g, const EpiArgs& e, int rows0,
+                                                int k0, int batch) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) unit_load<OPT, WT, ST>(x[r], unit_index(g, rows0, k0, 4 * batch + r), e);
+}
+
+// The stochastic-rounding words of a batch (zero when they are not used).
+template <int WT>
+__device__ __forceinline__ void unit_batch_words(uint64_t (&w)[4], const GemmArgs& g, const EpiArgs& e, int rows0,
+                                                 int k0, int batch) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w[r] = 0ull;
+  if (WT == FORGE_W_BF16 && e.sr) {
+    uint32_t i[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) i[r] = unit_index(g, rows0, k0, 4 * batch + r);
+    sr_words4(i, e, w);
+  }
+}
+
+template <int OPT, int WT, int ST>
+__device__ __forceinline__ void unit_batch_apply(const UnitIn (&x)[4], const uint64_t (&w)[4], const float* st,
+                                                 const GemmArgs& g, const EpiArgs& e, int rows0, int k0, int batch) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const floatx4 q = *reinterpret_cast<const floatx4*>(st + unit_row(4 * batch + r) * ml2::EPI_LD + unit_col());
+    const float gr[4] = {q[0], q[1], q[2], q[3]};
+    unit_apply<OPT, WT, ST>(gr, unit_index(g, rows0, k0, 4 * batch + r), x[r], w[r], e);
+  }
+}
+
+// The whole epilogue of a tile of HALVES x 128 rows: stage(h) writes rows [128 h, 128 h + 128)
+// into the staging.  The next batch's stored state is in flight while one is updated; the
+// first batch's loads leave before the first staging.
+template <int OPT, int WT, int ST, int HALVES, class Stage>
+__device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                              int k0, Stage&& stage) {
   float* st = reinterpret_cast<float*>(smem);
-  auto index_of = [&](int j) {  // flat W index of the thread's j-th segment (j = 4 half + s)
-    int row, kseg;
-    seg_pos(j & 3, row, kseg);
-    return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+  UnitIn xa[4], xb[4];
+  // one batch: words, the next batch's loads, then this batch's updates
+  auto batch = [&](UnitIn (&cur)[4], UnitIn (&nxt)[4], int h, int b) {
+    const int rows0 = n0 + 128 * h;
+    uint64_t w[4];
+    unit_batch_words<WT>(w, g, e, rows0, k0, b);
+    if (b < 3) unit_batch_load<OPT, WT, ST>(nxt, g, e, rows0, k0, b + 1);
+    else if (h + 1 < HALVES) unit_batch_load<OPT, WT, ST>(nxt, g, e, rows0 + 128, k0, 0);
+    unit_batch_apply<OPT, WT, ST>(cur, w, st, g, e, rows0, k0, b);
   };
-  constexpr bool kDeep0 = DEEP0;
-  SegIn x0, x1;
-  seg_load<OPT, WT, ST>(x0, index_of(0), e);
-  if constexpr (kDeep0) seg_load<OPT, WT, ST>(x1, index_of(1), e);
+  unit_batch_load<OPT, WT, ST>(xa, g, e, n0, k0, 0);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    stage(half);
+  for (int h = 0; h < HALVES; ++h) {
+    stage(h);
     __syncthreads();
-    if (half == 0 && !kDeep0) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float gr[16];
-        staged_grad(st, s, gr);
-        seg_apply<OPT, WT, ST>(gr, index_of(s), x0, e);
-        if (s < 3) seg_load<OPT, WT, ST>(x0, index_of(s + 1), e);
-      }
-      seg_load<OPT, WT, ST>(x0, index_of(4), e);
-      seg_load<OPT, WT, ST>(x1, index_of(5), e);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; s += 2) {
-        const int j = 4 * half + s;
-        float gr[16];
-        staged_grad(st, s, gr);
-        seg_apply<OPT, WT, ST>(gr, index_of(j), x0, e);
-        if (j + 2 < 8) seg_load<OPT, WT, ST>(x0, index_of(j + 2), e);
-        staged_grad(st, s + 1, gr);
-        seg_apply<OPT, WT, ST>(gr, index_of(j + 1), x1, e);
-        if (j + 3 < 8) seg_load<OPT, WT, ST>(x1, index_of(j + 3), e);
-      }
-    }
+    batch(xa, xb, h, 0);
+    batch(xb, xa, h, 1);
+    batch(xa, xb, h, 2);
+    batch(xb, xa, h, 3);
     __syncthreads();
   }
 }
 
+// Full 256 x 128 tile: contraction, then the epilogue over its two 128-row halves.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
   int nb, kb;
@@ -172,12 +203,10 @@ __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  full_tile_epilogue<WT, ST, OPT, WT == FORGE_W_BF16 && ST == FORGE_S_F32>(
-      g, e, smem, n0, k0, [&](int half) { ml2::stage_acc_half(st, acc, 1.0f, half); });
+  unit_epilogue<OPT, WT, ST, 2>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
 }
 
-// Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once, two
-// segments in flight.
+// Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
   int nb, kb;
@@ -186,26 +215,7 @@ __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs
   ml2::floatx4 acc[4][4];
   ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  auto index_of = [&](int s) {
-    int row, kseg;
-    seg_pos(s, row, kseg);
-    return (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
-  };
-  SegIn x0, x1;
-  seg_load<OPT, WT, ST>(x0, index_of(0), e);
-  seg_load<OPT, WT, ST>(x1, index_of(1), e);
-  ml2::stage_acc_all(st, acc, 1.0f);
-  __syncthreads();
-#pragma unroll
-  for (int s = 0; s < 4; s += 2) {
-    float gr[16];
-    staged_grad(st, s, gr);
-    seg_apply<OPT, WT, ST>(gr, index_of(s), x0, e);
-    if (s + 2 < 4) seg_load<OPT, WT, ST>(x0, index_of(s + 2), e);
-    staged_grad(st, s + 1, gr);
-    seg_apply<OPT, WT, ST>(gr, index_of(s + 1), x1, e);
-    if (s + 3 < 4) seg_load<OPT, WT, ST>(x1, index_of(s + 3), e);
-  }
+  unit_epilogue<OPT, WT, ST, 1>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
 }
 
 template <int WT, int ST, int OPT>
@@ -271,8 +281,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmAr
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
   float* st = reinterpret_cast<float*>(smem);
-  full_tile_epilogue<WT, ST, OPT, false>(g, e, smem, n0, k0,
-                                         [&](int half) { ml8::stage_acc_half(st, acc, scale, half); });
+  unit_epilogue<OPT, WT, ST, 2>(g, e, smem, n0, k0, [&](int h) { ml8::stage_acc_half(st, acc, scale, h); });
 }
 
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmArgs g, float* dW) {
@@ -331,20 +340,30 @@ static bool use_v8(int in_type, const GemmArgs& g) {
   return in_type == FORGE_IN_FP8 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
 }
 
-// Element-wise rule over a materialised gradient: one thread per 16 consecutive elements.
+// Element-wise rule over a materialised gradient, in the lane-contiguous unit layout of the
+// fused epilogue: a wave updates 1024 consecutive elements in 4 rounds of 256 (lane l holds
+// elements 256 r + 4 l .. + 3 of round r).  N K is a multiple of 16384, so whole waves (and the
+// quads and 16-lane int8 blocks inside them) are either in range or out of it.
 template <int WT, int ST, int OPT>
-__global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t nseg, EpiArgs e) {
-  const int64_t seg = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (seg >= nseg) return;  // nseg % 4 == 0, so the 4 lanes of an int8 block leave together
-  float g[16];
-  const float* p = dW + seg * 16;
+__global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t n_elem, EpiArgs e) {
+  const int64_t base = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * 1024;
+  if (base >= n_elem) return;
+  const int lane = (int)(threadIdx.x & 63);
+  uint32_t i[4];
+  UnitIn x[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 x = ld16(p + 4 * q);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[4 * q + c] = __uint_as_float(x[c]);
+  for (int r = 0; r < 4; ++r) {
+    i[r] = (uint32_t)(base + 256 * r + 4 * lane);
+    unit_load<OPT, WT, ST>(x[r], i[r], e);
   }
-  step_segment16<OPT, WT, ST>(g, (uint32_t)(seg * 16), e);
+  uint64_t w[4] = {0ull, 0ull, 0ull, 0ull};
+  if (WT == FORGE_W_BF16 && e.sr) sr_words4(i, e, w);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x4 q = ld16(dW + i[r]);
+    const float gr[4] = {__uint_as_float(q[0]), __uint_as_float(q[1]), __uint_as_float(q[2]), __uint_as_float(q[3])};
+    unit_apply<OPT, WT, ST>(gr, i[r], x[r], w[r], e);
+  }
 }
 
 // dX[T, K] = dY[T, N] . W[N, K], bf16 in, fp32 accumulate, bf16 (nearest-even) out.
@@ -524,9 +543,8 @@ int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n
   else
     fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_F32, FORGE_S_F32>(opt) : opt_for<FORGE_W_F32, FORGE_S_Q8>(opt);
   if (!fn) return (int)hipErrorInvalidValue;
-  const int64_t nseg = n_elem / 16;
-  const unsigned grid = (unsigned)((nseg + 255) / 256);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, dW, nseg, e);
+  const unsigned grid = (unsigned)((n_elem + 4095) / 4096);   // 4 waves of 1024 elements a block
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, dW, n_elem, e);
   return (int)hipGetLastError();
 }
 

@@ -153,6 +153,16 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char* panel, int row_bytes
   return __builtin_bit_cast(bf16x8, x);
 }
 
+// Tile row of a wave's MFMA row block bi.  Full tiles (MB = 8): the wave's 8 blocks are two
+// groups of 4, one in each 128-row half of the tile (rows 64 wm .. of each half), so that each
+// half of the epilogue stages 4 blocks of every wave and frees their registers.  Half tiles
+// (MB = 4): rows 64 wm + 16 bi.
+template <int MB>
+__device__ __forceinline__ int a_row(int wm, int bi) {
+  if constexpr (MB == 8) return 128 * (bi >> 2) + 64 * wm + 16 * (bi & 3);
+  return 64 * wm + 16 * bi;
+}
+
 template <class P>
 __device__ __forceinline__ void mma_stage(floatx4 (&acc)[P::MB][4], const unsigned char* stage, int wm, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
@@ -166,7 +176,7 @@ __device__ __forceinline__ void mma_stage(floatx4 (&acc)[P::MB][4], const unsign
     for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, ROW_B, r0, r1, wn * 64 + 16 * bj, i);
 #pragma unroll
     for (int bi = 0; bi < P::MB; ++bi) {
-      const bf16x8 a = frag(pa, P::ROW_A, r0, r1, wm * 16 * P::MB + 16 * bi, i);
+      const bf16x8 a = frag(pa, P::ROW_A, r0, r1, a_row<P::MB>(wm, bi), i);
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
     }
@@ -208,18 +218,21 @@ __device__ __forceinline__ void contract(floatx4 (&acc)[P::MB][4], unsigned char
 }
 
 // Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
-// [128][EPI_LD], multiplied by `scale`; the waves holding those rows write them.
+// [128][EPI_LD], multiplied by `scale`: every wave writes its blocks 4 half .. 4 half + 3.
 __device__ __forceinline__ void stage_acc_half(float* st, const floatx4 (&acc)[8][4], float scale, int half) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
-  if (wm != half) return;
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi)
+  for (int hb = 0; hb < 2; ++hb) {
+    if (hb != half) continue;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int b4 = 0; b4 < 4; ++b4)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        st[(16 * bi + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[bi][bj][r] * scale;
+      for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st[(64 * wm + 16 * b4 + 4 * q + r) * EPI_LD + wn * 64 + 16 * bj + r16] = acc[4 * hb + b4][bj][r] * scale;
+  }
 }
 
 // Stage all 128 rows of a half tile's accumulators in LDS as fp32 [128][EPI_LD], times `scale`.
@@ -316,7 +329,7 @@ __device__ __forceinline__ void dgrad_mma_stage(floatx4 (&acc)[8][4], const unsi
   for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, ROW_B, r0, r1, wn * 64 + 16 * bj, i);
 #pragma unroll
   for (int bi = 0; bi < 8; ++bi) {
-    const bf16x8 a = dy_frag(pa, wm * 128 + 16 * bi + i, q);
+    const bf16x8 a = dy_frag(pa, a_row<8>(wm, bi) + i, q);
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
   }

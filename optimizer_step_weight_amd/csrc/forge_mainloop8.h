@@ -112,7 +112,7 @@ __device__ __forceinline__ void mma_stage(floatx16 (&acc)[4][2], const unsigned 
   for (int bj = 0; bj < 2; ++bj) b[bj] = frag<false>(pb, wn * 64 + 32 * bj);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
-    const intx8 a = frag<true>(pa, wm * 128 + 32 * bi);
+    const intx8 a = frag<true>(pa, 128 * (bi >> 1) + 64 * wm + 32 * (bi & 1));
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj)
       acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[bj], acc[bi][bj], 0, 0, 0, 127, 0, 127);
@@ -148,19 +148,25 @@ __device__ __forceinline__ void contract(floatx16 (&acc)[4][2], unsigned char* s
 }
 
 // Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
-// [128][EPI_LD], times `scale`.  32 x 32 output layout: register v of lane l holds row
-// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+// [128][EPI_LD], times `scale`.  A wave's 32-row blocks bi are rows 128 (bi / 2) + 64 wm +
+// 32 (bi % 2) of the tile (two in each half, so each half frees half of every wave's
+// accumulators).  32 x 32 output layout: register v of lane l holds row 8 (v / 4) + 4 (l / 32) +
+// v % 4, column l % 32 of its block.
 __device__ __forceinline__ void stage_acc_half(float* st, const floatx16 (&acc)[4][2], float scale, int half) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
-  if (wm != half) return;
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+  for (int hb = 0; hb < 2; ++hb) {
+    if (hb != half) continue;
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        st[(32 * bi + 8 * (v >> 2) + 4 * h + (v & 3)) * ml2::EPI_LD + wn * 64 + 32 * bj + c32] = acc[bi][bj][v] * scale;
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          st[(64 * wm + 32 * b2 + 8 * (v >> 2) + 4 * h + (v & 3)) * ml2::EPI_LD + wn * 64 + 32 * bj + c32] =
+              acc[2 * hb + b2][bj][v] * scale;
+  }
 }
 
 }  // namespace ml8
