@@ -194,6 +194,50 @@ __device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& 
   }
 }
 
+// Segment epilogue: 16 consecutive elements of a row per thread (4 per 128-row half), the
+// stored state of the next two segments in flight while one is updated.  Used for int8
+// moments: with 1-byte codes and per-block scales the 4-element units take about 3x more
+// small memory instructions per element than 16-element segments, and the contiguous-lane
+// layout gains little on such narrow data.
+template <int OPT, int WT, int ST, int HALVES, class Stage>
+__device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                             int k0, Stage&& stage) {
+  float* st = reinterpret_cast<float*>(smem);
+  auto index_of = [&](int j) {  // the thread's j-th segment (j = 4 half + s)
+    int row, kseg;
+    seg_pos(j & 3, row, kseg);
+    return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+  };
+  // one segment in flight: the int8 update needs more registers than the fp32 one, and the
+  // accumulators of the second half are still live during the first
+  SegIn x0;
+  seg_load<OPT, WT, ST>(x0, index_of(0), e);
+#pragma unroll
+  for (int h = 0; h < HALVES; ++h) {
+    stage(h);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int j = 4 * h + s;
+      float gr[16];
+      staged_grad(st, s, gr);
+      seg_apply<OPT, WT, ST>(gr, index_of(j), x0, e);
+      if (j + 1 < 4 * HALVES) seg_load<OPT, WT, ST>(x0, index_of(j + 1), e);
+    }
+    __syncthreads();
+  }
+}
+
+// The epilogue for the state format: 4-element units for fp32 moments, segments for int8
+// (SEG_INT8; the fp8 kernel keeps units for int8, where the segment form does not fit its
+// registers).
+template <int OPT, int WT, int ST, int HALVES, bool SEG_INT8, class Stage>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                              int k0, Stage&& stage) {
+  if constexpr (ST == FORGE_S_Q8 && SEG_INT8) seg_epilogue<OPT, WT, ST, HALVES>(g, e, smem, n0, k0, stage);
+  else unit_epilogue<OPT, WT, ST, HALVES>(g, e, smem, n0, k0, stage);
+}
+
 // Full 256 x 128 tile: contraction, then the epilogue over its two 128-row halves.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
@@ -203,7 +247,7 @@ __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  unit_epilogue<OPT, WT, ST, 2>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
+  tile_epilogue<OPT, WT, ST, 2, true>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
 }
 
 // Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once.
@@ -215,7 +259,7 @@ __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs
   ml2::floatx4 acc[4][4];
   ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
-  unit_epilogue<OPT, WT, ST, 1>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
+  tile_epilogue<OPT, WT, ST, 1, true>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
 }
 
 template <int WT, int ST, int OPT>
@@ -281,7 +325,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmAr
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
   float* st = reinterpret_cast<float*>(smem);
-  unit_epilogue<OPT, WT, ST, 2>(g, e, smem, n0, k0, [&](int h) { ml8::stage_acc_half(st, acc, scale, h); });
+  tile_epilogue<OPT, WT, ST, 2, false>(g, e, smem, n0, k0, [&](int h) { ml8::stage_acc_half(st, acc, scale, h); });
 }
 
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmArgs g, float* dW) {
@@ -340,12 +384,26 @@ static bool use_v8(int in_type, const GemmArgs& g) {
   return in_type == FORGE_IN_FP8 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
 }
 
-// Element-wise rule over a materialised gradient, in the lane-contiguous unit layout of the
-// fused epilogue: a wave updates 1024 consecutive elements in 4 rounds of 256 (lane l holds
-// elements 256 r + 4 l .. + 3 of round r).  N K is a multiple of 16384, so whole waves (and the
+// Element-wise rule over a materialised gradient, in the layout of the fused epilogue for the
+// state format.  fp32 moments: lane-contiguous units, a wave updates 1024 consecutive elements
+// in 4 rounds of 256 (lane l holds elements 256 r + 4 l .. + 3 of round r); int8 moments: 16
+// consecutive elements per thread.  N K is a multiple of 16384, so whole waves (and the
 // quads and 16-lane int8 blocks inside them) are either in range or out of it.
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t n_elem, EpiArgs e) {
+  if constexpr (ST == FORGE_S_Q8) {  // int8 moments: 16 consecutive elements per thread (see seg_epilogue)
+    const int64_t seg = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (seg * 16 >= n_elem) return;  // n_elem % 64 == 0: the 4 lanes of an int8 block leave together
+    float gr[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 x = ld16(dW + seg * 16 + 4 * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gr[4 * q + c] = __uint_as_float(x[c]);
+    }
+    step_segment16<OPT, WT, ST>(gr, (uint32_t)(seg * 16), e);
+    return;
+  }
   const int64_t base = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * 1024;
   if (base >= n_elem) return;
   const int lane = (int)(threadIdx.x & 63);
