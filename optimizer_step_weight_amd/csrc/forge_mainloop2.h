@@ -22,10 +22,11 @@
 //    global address each DMA lane fetches; the transpose reads of 8 consecutive token rows
 //    then hit 8 disjoint bank groups.
 //
-// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k).  Full tiles are 256 x 128 (wave tile
-// 128 x 64 = 8 x 4 MFMA 16x16x32 blocks, 128 accumulator registers per lane); half tiles are
-// 128 x 128 (wave tile 64 x 64) and balance the last round of a launch (see the launcher).
-// Two workgroups per CU.
+// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k).  Full tiles are 256 x 128: a wave holds
+// 8 x 4 MFMA 16x16x32 blocks (128 accumulator registers per lane) of 64 columns and 128 rows,
+// rows 64 wm .. 64 wm + 63 of each 128-row half of the tile (a_row), so that each half of the
+// epilogue frees half of every wave's accumulators.  Half tiles are 128 x 128 (wave tile
+// 64 x 64) and balance the last round of a launch (see the launcher).  Two workgroups per CU.
 #pragma once
 
 #include <hip/hip_runtime.h>

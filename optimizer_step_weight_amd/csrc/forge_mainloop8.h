@@ -23,8 +23,9 @@
 //    256-byte dY rows (one row spans all 64 banks), chunk ^ 2 ((t / 2) mod 4) in the
 //    128-byte X rows (two rows share the 64 banks).
 //
-// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k), wave tile 128 x 64 = 4 x 2 MFMA 32 x 32
-// blocks (16 accumulators each, 128 registers per lane), two workgroups per CU.
+// Workgroup: 256 threads = 4 waves as 2 (n) x 2 (k); a wave holds 4 x 2 MFMA 32 x 32 blocks
+// (16 accumulators each, 128 registers per lane) of 64 columns and 128 rows, two 32-row blocks
+// in each 128-row half of the tile (as on the bf16 path), two workgroups per CU.
 #pragma once
 
 #include "forge_mainloop2.h"
