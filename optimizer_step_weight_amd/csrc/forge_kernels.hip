@@ -94,9 +94,13 @@ constexpr int kOcc2 = 2;
 constexpr int kSmem2 = Pipe2::SMEM;
 static_assert(Pipe2H::SMEM <= kSmem2 && ml2::EPI_BYTES <= kSmem2, "half tiles and the staging share the LDS");
 
+// Epilogue helpers index threads within a group of 256 (a whole 256-thread workgroup, or one
+// 128-column half of an 8-wave workgroup).
+__device__ __forceinline__ int group_tid() { return (int)(threadIdx.x & (ml2::THREADS - 1)); }
+
 // The thread's 16-element segment s (0..3) of 128 staged rows: row and column in the staging.
 __device__ __forceinline__ void seg_pos(int s, int& row, int& kseg) {
-  const int seg = threadIdx.x + ml2::THREADS * s;
+  const int seg = group_tid() + ml2::THREADS * s;
   row = seg >> 3;
   kseg = seg & 7;
 }
@@ -465,6 +469,51 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void dgrad_kernel2(const uint1
   }
 }
 
+// dX tiles of 256 tokens x 256 columns, one workgroup of 8 waves per CU (forge_mainloop2.h, wide
+// dgrad tiles): both 128-column halves share the dY slab and 4 slabs fit in LDS.  Each half
+// stages its accumulators through its own LDS buffer and stores bf16 rows as dgrad_kernel2 does.
+constexpr int kSmemDW =
+    ml2::DgradWidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::DgradWidePipe::SMEM : 2 * ml2::EPI_BYTES;
+static_assert(kSmemDW <= 160 * 1024, "wide dgrad tiles fit the CU's LDS");
+
+__global__ __launch_bounds__(2 * ml2::THREADS, 1) void dgrad_kernel2w(const uint16_t* dY, const uint16_t* W,
+                                                                       uint16_t* dX, int64_t T, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemDW];
+  const int nbT = (int)((T + ml2::BM - 1) / ml2::BM), nbK2 = (int)(K / (2 * ml2::BN));
+  int tb, kb;
+  tile_coords_at((int)blockIdx.x, nbT, nbK2, tb, kb);
+  const int64_t t0 = (int64_t)tb * ml2::BM;
+  const int kh = (int)(threadIdx.x >> 8);
+  const int k0 = (2 * kb + kh) * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::dgrad_wide_contract(acc, smem, dY, W, T, N, K, t0, 2 * kb * ml2::BN);
+  float* st = reinterpret_cast<float*>(smem + kh * ml2::EPI_BYTES);
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    ml2::stage_acc_half(st, acc, 1.0f, half);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int row, kseg;
+      seg_pos(s, row, kseg);
+      const int64_t t = t0 + half * ml2::EPI_ROWS + row;
+      if (t >= T) continue;
+      float gr[16];
+      staged_grad(st, s, gr);
+      u32x4 a, b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
+        b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
+      }
+      uint16_t* d = dX + t * K + k0 + kseg * 16;
+      st16(d, a);
+      st16(d + 8, b);
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ dispatch tables
 using FusedFn = void (*)(GemmArgs, EpiArgs);
 using OptFn = void (*)(const float*, int64_t, EpiArgs);
@@ -606,7 +655,20 @@ int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n
   return (int)hipGetLastError();
 }
 
+// Wide dgrad tiles need K % 256 == 0 and at least one tile per CU.
+static bool use_dgrad_wide(int64_t T, int64_t K) {
+  const int64_t tiles = ((T + ml2::BM - 1) / ml2::BM) * (K / (2 * ml2::BN));
+  return K % (2 * ml2::BN) == 0 && tiles >= slots_on_current_device() / 2;
+}
+
 int launch_dgrad(const void* dY, const void* W, void* dX, int64_t T, int64_t N, int64_t K, void* stream) {
+  if (use_dgrad_wide(T, K)) {
+    const unsigned gridw = (unsigned)(((T + ml2::BM - 1) / ml2::BM) * (K / (2 * ml2::BN)));
+    hipLaunchKernelGGL(dgrad_kernel2w, dim3(gridw), dim3(2 * ml2::THREADS), 0, (hipStream_t)stream,
+                       static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(dX),
+                       T, N, K);
+    return (int)hipGetLastError();
+  }
   const unsigned grid = (unsigned)(((T + ml2::BM - 1) / ml2::BM) * (K / ml2::BN));
   hipLaunchKernelGGL(dgrad_kernel2, dim3(grid), dim3(ml2::THREADS), 0, (hipStream_t)stream,
                      static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(dX), T,

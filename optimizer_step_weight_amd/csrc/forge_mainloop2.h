@@ -219,9 +219,10 @@ __device__ __forceinline__ void contract(floatx4 (&acc)[P::MB][4], unsigned char
 }
 
 // Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
-// [128][EPI_LD], multiplied by `scale`: every wave writes its blocks 4 half .. 4 half + 3.
+// [128][EPI_LD], multiplied by `scale`: every wave writes its blocks 4 half .. 4 half + 3.  In
+// an 8-wave workgroup each group of 4 waves stages its 128 columns into its own buffer.
 __device__ __forceinline__ void stage_acc_half(float* st, const floatx4 (&acc)[8][4], float scale, int half) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
@@ -358,6 +359,103 @@ __device__ __forceinline__ void dgrad_contract(floatx4 (&acc)[8][4], unsigned ch
     barrier();
     if (s + P::STAGES - 1 < nsl) dgrad_issue(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
     dgrad_mma_stage(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn);
+  }
+  barrier();
+}
+
+// ------------------------------------------------------------------ wide dgrad tiles
+// dX tiles of 256 tokens x 256 columns in one workgroup of 8 waves: waves 0-3 compute columns
+// k0 .. k0 + 127 and waves 4-7 columns k0 + 128 .. k0 + 255, each with the wave layout above.
+// Both halves read the same dY slab (256 token rows of 32 n), so a slab moves 16 KiB of dY and
+// 16 KiB of W (32 rows of 256 columns) and 4 stages fit in 128 KiB.  Every element's sum runs
+// over n in the same order as on the 256 x 128 path, so both give bitwise the same dX.
+struct DgradWidePipe {
+  static constexpr int TK = 32, STAGES = 4;
+  static constexpr int ROW_D = TK * 2;                   // dY bytes per token row (64)
+  static constexpr int ROW_W = 512;                      // W bytes per row of n (256 columns)
+  static constexpr int PANEL_A = 256 * ROW_D, PANEL_B = TK * ROW_W;   // 16 KiB each
+  static constexpr int STAGE = PANEL_A + PANEL_B, SMEM = STAGES * STAGE;
+  static constexpr int DMA = 4;                          // per wave per slab: 2 of dY, 2 of W
+};
+
+struct DgradWideFeed {
+  u32x4 rA, rB;
+  uint32_t offA[2], offB[2];
+  uint32_t stepA, stepB;
+};
+
+// Wave w (0..7) moves dY token rows 32 w .. 32 w + 31 (a 1 KiB DMA is 16 rows of 4 chunks) and
+// W rows 4 w .. 4 w + 3 (a 1 KiB DMA is 2 rows of 32 chunks).
+__device__ __forceinline__ void make_dgrad_wide_feed(DgradWideFeed& f, const void* dY, const void* W, int64_t T,
+                                                     int64_t N, int64_t K, int64_t t0, int k0) {
+  using P = DgradWidePipe;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(dY, (uint32_t)(T * N * 2));
+  f.rB = make_rsrc(W, (uint32_t)(N * K * 2));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ra = 16 * (2 * wave + j) + (lane >> 2), pa = lane & 3;
+    f.offA[j] = (uint32_t)((t0 + ra) * N * 2 + 16 * (pa ^ swz_d(ra)));
+    const int rb = 2 * (2 * wave + j) + (lane >> 5), pb = lane & 31;
+    f.offB[j] = (uint32_t)(rb * K * 2 + k0 * 2 + 16 * (pb ^ swz(rb)));
+  }
+  f.stepA = (uint32_t)(P::TK * 2);
+  f.stepB = (uint32_t)(P::TK * K * 2);
+}
+
+__device__ __forceinline__ void dgrad_wide_issue(const DgradWideFeed& f, unsigned char* stage, int slab) {
+  using P = DgradWidePipe;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rA, f.offA[j] + sa, stage + (2 * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rB, f.offB[j] + sb, stage + P::PANEL_A + (2 * wave + j) * 1024);
+}
+
+__device__ __forceinline__ void dgrad_wide_mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm,
+                                                     int wn, int kh) {
+  using P = DgradWidePipe;
+  const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + P::PANEL_A;
+  const int r0 = 4 * q + (i >> 2), r1 = r0 + 16;
+  bf16x8 b[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, P::ROW_W, r0, r1, kh * 128 + wn * 64 + 16 * bj, i);
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi) {
+    const bf16x8 a = dy_frag(pa, a_row<8>(wm, bi) + i, q);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
+  }
+}
+
+// acc = this wave's part of dX for the 256-token x 256-column tile at (t0, k0).  Ends with a
+// barrier (LDS free for reuse).
+__device__ __forceinline__ void dgrad_wide_contract(floatx4 (&acc)[8][4], unsigned char* smem, const void* dY,
+                                                    const void* W, int64_t T, int64_t N, int64_t K, int64_t t0,
+                                                    int k0) {
+  using P = DgradWidePipe;
+  const int wave = threadIdx.x >> 6, kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  DgradWideFeed f;
+  make_dgrad_wide_feed(f, dY, W, T, N, K, t0, k0);
+  const int nsl = (int)(N / P::TK);
+#pragma unroll
+  for (int s = 0; s < P::STAGES - 1; ++s)
+    if (s < nsl) dgrad_wide_issue(f, smem + s * P::STAGE, s);
+  for (int s = 0; s < nsl; ++s) {
+    const int ahead = min(nsl - 1 - s, P::STAGES - 2);
+    if (ahead >= 2) wait_vm<2 * P::DMA>();
+    else if (ahead == 1) wait_vm<P::DMA>();
+    else wait_vm<0>();
+    barrier();
+    if (s + P::STAGES - 1 < nsl) dgrad_wide_issue(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
+    dgrad_wide_mma_stage(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn, kh);
   }
   barrier();
 }

@@ -234,6 +234,30 @@ def test_dgrad_matches_oracle(lib, Tn, Nn, Kn):
     P.dx_close(got, wgrad.decode_operand(dY), numerics.bf16_to_f64(W))
 
 
+# 256-token x 256-column dX tiles in one 8-wave workgroup per CU are used when K % 256 == 0 and
+# there are at least as many of them as CUs (256 on an MI355X): 4196 x 4096 is 17 x 16 = 272
+# tiles with a ragged last token block, 2048 x 8192 is 8 x 32 = 256.  4196 x 4224 (K / 128 odd)
+# stays on the 256 x 128 tiles.  Same two checks as above: exact sums bitwise, Gaussian within
+# the summation bound.
+@pytest.mark.parametrize("Tn,Nn,Kn", [(4196, 256, 4096), (2048, 384, 8192), (4196, 256, 4224)])
+def test_dgrad_wide_tiles_match_oracle(lib, Tn, Nn, Kn):
+    _say("dgrad wide", Tn, Nn, Kn)
+    _, dY = synth.integer_case(90, Tn, Nn, 128, "bf16")
+    Wi, _ = synth.integer_case(91, Nn, 128, Kn, "bf16")
+    dYd, _ = P.dev_operand(dY)
+    dX = torch.empty((Tn, Kn), dtype=torch.bfloat16, device="cuda")
+    lib.dgrad(dYd, P.dev_weight(Wi.data, "bf16"), dX)
+    ref = wgrad.dgrad_bf16(wgrad.decode_operand(dY), numerics.bf16_to_f64(Wi.data))
+    got = dX.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    _, dY = synth.gaussian_case(92, Tn, Nn, 128, "bf16")
+    W = synth.random_weight(93, Nn, Kn, "bf16")
+    dYd, _ = P.dev_operand(dY)
+    lib.dgrad(dYd, P.dev_weight(W, "bf16"), dX)
+    got = dX.view(torch.int16).cpu().numpy().view(np.uint16)
+    P.dx_close(got, wgrad.decode_operand(dY), numerics.bf16_to_f64(W))
+
+
 def test_backward_step_reads_the_old_weight(lib):
     """dX must see W before the update (limitation stated in the explainer's section 5)."""
     _say("ordering")
