@@ -127,7 +127,7 @@ __device__ __forceinline__ void staged_grad(const float* st, int s, float (&gr)[
 // 8 rho + 2 wave + lane / 32, columns 4 (lane % 32) .. +3, so a wave touches two contiguous row
 // segments per access.  Batches of 4 rounds share one Philox block per quad.
 __device__ __forceinline__ int unit_row(int rho) {
-  return 8 * rho + 2 * (int)(threadIdx.x >> 6) + (int)((threadIdx.x & 63) >> 5);
+  return 8 * rho + 2 * (group_tid() >> 6) + ((group_tid() & 63) >> 5);
 }
 __device__ __forceinline__ int unit_col() { return 4 * (int)(threadIdx.x & 31); }
 
@@ -247,19 +247,19 @@ template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
   int nb, kb;
   tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
-  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
   tile_epilogue<OPT, WT, ST, 2, true>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
 }
 
-// Half 128 x 128 tile hb of the columns [kb_split, K / 128): all 128 rows staged at once.
+// Half 128 x 128 tile hb of the blocks [kb_split, nbk): all 128 rows staged at once.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
   int nb, kb;
-  tile_coords_at(hb, (int)(g.N / ml2::BM_HALF), (int)(g.K / ml2::BN) - g.kb_split, nb, kb);
-  const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_split + kb) * ml2::BN;
+  tile_coords_at(hb, (int)(g.N / ml2::BM_HALF), g.nbk - g.kb_split, nb, kb);
+  const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
   ml2::floatx4 acc[4][4];
   ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
@@ -272,6 +272,29 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
   const int b = (int)blockIdx.x;
   if (b < g.nfull) fused_full_tile<WT, ST, OPT>(g, e, smem, b);
   else fused_half_tile<WT, ST, OPT>(g, e, smem, b - g.nfull);
+}
+
+// bf16 inputs, 256 x 256 tiles, one workgroup of 8 waves per CU (forge_mainloop2.h, wide
+// tiles): both 128-column halves share the dY panel and 4 slabs fit in LDS.  The epilogue is
+// the 256 x 128 tile's, run by each half: threads 0-255 update columns k0 .. k0 + 127 and
+// threads 256-511 columns k0 + 128 .. k0 + 255, each staging through its own LDS buffer.  The
+// launch covers the nbk / 2 wide column blocks from kb_base / 2 on.
+constexpr int kSmemW = ml2::WidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::WidePipe::SMEM : 2 * ml2::EPI_BYTES;
+static_assert(kSmemW <= 160 * 1024, "wide tiles fit the CU's LDS");
+
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel2w(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemW];
+  int nb, kb;
+  tile_coords_at((int)blockIdx.x, (int)(g.N / ml2::BM), g.nbk / 2, nb, kb);
+  const int kh = (int)(threadIdx.x >> 8);
+  const int n0 = nb * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract_wide(acc, smem, g, n0, kw0);
+  unsigned char* mine = smem + kh * ml2::EPI_BYTES;
+  float* st = reinterpret_cast<float*>(mine);
+  tile_epilogue<OPT, WT, ST, 2, true>(g, e, mine, n0, kw0 + kh * ml2::BN,
+                                      [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
 }
 
 // dW rows of 128 staged rows, written with 16-byte stores.
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
   int nb, kb;
   if (b < g.nfull) {
     tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
-    const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+    const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
     ml2::floatx4 acc[8][4];
     ml2::contract<Pipe2>(acc, smem, g, n0, k0);
 #pragma unroll 1
@@ -305,8 +328,8 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
       __syncthreads();
     }
   } else {
-    tile_coords_at(b - g.nfull, (int)(g.N / ml2::BM_HALF), (int)(g.K / ml2::BN) - g.kb_split, nb, kb);
-    const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_split + kb) * ml2::BN;
+    tile_coords_at(b - g.nfull, (int)(g.N / ml2::BM_HALF), g.nbk - g.kb_split, nb, kb);
+    const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
     ml2::floatx4 acc[4][4];
     ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
     ml2::stage_acc_all(st, acc, 1.0f);
@@ -368,13 +391,26 @@ static int slots_on_current_device() {
 // into 128 x 128 half tiles (c = the fewest columns that hold that remainder) ends the launch
 // with a round of half tiles instead.  Returns the grid size.
 static unsigned plan_split(GemmArgs& g) {
-  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
+  const int nbN = (int)(g.N / ml2::BM), nbK = g.nbk;
   const int full = nbN * nbK, slots = slots_on_current_device();
   const int rem = full % slots;
   const int c = rem == 0 ? 0 : std::min(nbK, (rem + nbN - 1) / nbN);
   g.kb_split = nbK - c;
   g.nfull = nbN * g.kb_split;
   return (unsigned)(g.nfull + 2 * nbN * c);
+}
+
+// Wide 256 x 256 tiles for long token counts (T >= 8192, where the faster contraction outweighs
+// the epilogue that no other workgroup on the CU overlaps; at T = 4096 both layouts take the same
+// time): the first kw 256-column blocks of every 256-row block, kw the largest count for which
+// N / 256 * kw is a positive multiple of the CU count; 0 otherwise.  The remaining columns run on
+// the 256 x 128 path.
+static int plan_wide(const GemmArgs& g) {
+  if (g.T < 8192) return 0;
+  const int nbN = (int)(g.N / ml2::BM), nbK2 = (int)(g.K / (2 * ml2::BN)), cus = slots_on_current_device() / 2;
+  for (int kw = nbK2; kw > 0; --kw)
+    if ((nbN * kw) % cus == 0) return kw;
+  return 0;
 }
 
 // The 256 x 128 path needs N % 256 == 0 and at least 128 of its tiles (256 workgroups once the
@@ -571,6 +607,20 @@ static FusedFn fused_for(int w, int s, int opt) {
 }
 
 template <int WT, int ST>
+static FusedFn fused2w_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return fused_step_kernel2w<WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return fused_step_kernel2w<WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return fused_step_kernel2w<WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return fused_step_kernel2w<WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return fused_step_kernel2w<WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return fused_step_kernel2w<WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return fused_step_kernel2w<WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return fused_step_kernel2w<WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
+template <int WT, int ST>
 static OptFn opt_for(int opt) {
   switch (opt) {
     case FORGE_OPT_ADAMW: return optimizer_kernel<WT, ST, FORGE_OPT_ADAMW>;
@@ -589,12 +639,32 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
                       void* stream) {
   FusedFn fn = nullptr;
   if (use_v2(in_type, g)) {
-    if (w_type == FORGE_W_BF16)
+    FusedFn fw = nullptr;
+    if (w_type == FORGE_W_BF16) {
       fn = s_type == FORGE_S_F32 ? fused2_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused2_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
-    else
+      fw = s_type == FORGE_S_F32 ? fused2w_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused2w_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+    } else {
       fn = s_type == FORGE_S_F32 ? fused2_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused2_for<FORGE_W_F32, FORGE_S_Q8>(opt);
-    if (!fn) return (int)hipErrorInvalidValue;
+      fw = s_type == FORGE_S_F32 ? fused2w_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused2w_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+    }
+    if (!fn || !fw) return (int)hipErrorInvalidValue;
     GemmArgs g2 = g;
+    g2.kb_base = 0;
+    g2.nbk = (int)(g.K / ml2::BN);
+    // wide tiles first; the columns they leave go to the 256 x 128 path in a second launch
+    const int kw = plan_wide(g);
+    if (kw > 0) {
+      GemmArgs gw = g;
+      gw.kb_base = 0;
+      gw.nbk = 2 * kw;
+      const unsigned gridw = (unsigned)((g.N / ml2::BM) * kw);
+      hipLaunchKernelGGL(fw, dim3(gridw), dim3(2 * ml2::THREADS), 0, (hipStream_t)stream, gw, e);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return (int)err;
+      g2.kb_base = 2 * kw;
+      g2.nbk -= 2 * kw;
+      if (g2.nbk == 0) return (int)hipSuccess;
+    }
     const unsigned grid2 = plan_split(g2);
     hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, e);
     return (int)hipGetLastError();
@@ -621,6 +691,8 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
 int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
   if (use_v2(in_type, g)) {
     GemmArgs g2 = g;
+    g2.kb_base = 0;
+    g2.nbk = (int)(g.K / ml2::BN);
     const unsigned grid2 = plan_split(g2);
     hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, dW);
     return (int)hipGetLastError();

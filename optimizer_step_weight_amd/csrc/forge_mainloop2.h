@@ -218,6 +218,95 @@ __device__ __forceinline__ void contract(floatx4 (&acc)[P::MB][4], unsigned char
   barrier();
 }
 
+// ------------------------------------------------------------------ wide tiles (256 x 256)
+// One workgroup of 8 waves contracts a 256 x 256 tile: waves 0-3 the columns k0 .. k0 + 127
+// and waves 4-7 the columns k0 + 128 .. k0 + 255, each group with the wave layout of the
+// 256 x 128 tile above.  Both groups read the same dY panel, so a slab moves 16 KiB of dY and
+// 16 KiB of X (one third less than two 256 x 128 tiles), and 4 stages fit in 128 KiB.  Every
+// element's sum runs over the tokens in the same slab and k-slot order as on the 256 x 128
+// path, so both give bitwise the same gradient.
+struct WidePipe {
+  static constexpr int TK = 32, STAGES = 4, ROW = 512;   // 256 bf16 per token row, both panels
+  static constexpr int PANEL = TK * ROW, STAGE = 2 * PANEL, SMEM = STAGES * STAGE;
+  static constexpr int DMA = 4;                         // per wave per slab: 2 of dY, 2 of X
+};
+
+struct WideFeed {
+  u32x4 rA, rB;
+  uint32_t offA[2], offB[2];
+  uint32_t stepA, stepB;
+};
+
+// A 1 KiB DMA covers 2 token rows of 512 bytes (32 chunks of 16 bytes); wave w moves rows
+// 4 w .. 4 w + 3 of each panel.  Chunks are XOR-swizzled with 2 (t mod 8) as above.
+__device__ __forceinline__ void make_wide_feed(WideFeed& f, const GemmArgs& g, int n0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(g.dY, (uint32_t)(g.T * g.N * 2));
+  f.rB = make_rsrc(g.X, (uint32_t)(g.T * g.K * 2));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 2 * (2 * wave + j) + (lane >> 5), c = (lane & 31) ^ swz(r);
+    f.offA[j] = (uint32_t)(r * g.N * 2 + n0 * 2 + c * 16);
+    f.offB[j] = (uint32_t)(r * g.K * 2 + k0 * 2 + c * 16);
+  }
+  f.stepA = (uint32_t)(WidePipe::TK * g.N * 2);
+  f.stepB = (uint32_t)(WidePipe::TK * g.K * 2);
+}
+
+__device__ __forceinline__ void wide_issue(const WideFeed& f, unsigned char* stage, int slab) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rA, f.offA[j] + sa, stage + (2 * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rB, f.offB[j] + sb, stage + WidePipe::PANEL + (2 * wave + j) * 1024);
+}
+
+// The 256 x 128 tile's slab step on 512-byte rows; kh selects the 128-column half of X.
+__device__ __forceinline__ void wide_mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn,
+                                               int kh) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + WidePipe::PANEL;
+  const int r0 = 4 * q + (i >> 2), r1 = r0 + 16;
+  bf16x8 b[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, WidePipe::ROW, r0, r1, kh * 128 + wn * 64 + 16 * bj, i);
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi) {
+    const bf16x8 a = frag(pa, WidePipe::ROW, r0, r1, a_row<8>(wm, bi), i);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
+  }
+}
+
+// acc = this wave's part of dW for the 256 x 256 tile at (n0, k0).  Ends with a barrier.
+__device__ __forceinline__ void contract_wide(floatx4 (&acc)[8][4], unsigned char* smem, const GemmArgs& g, int n0,
+                                              int k0) {
+  using P = WidePipe;
+  const int wave = threadIdx.x >> 6, kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  WideFeed f;
+  make_wide_feed(f, g, n0, k0);
+  const int nsl = (int)((g.T + P::TK - 1) / P::TK);
+#pragma unroll
+  for (int s = 0; s < P::STAGES - 1; ++s)
+    if (s < nsl) wide_issue(f, smem + s * P::STAGE, s);
+  for (int s = 0; s < nsl; ++s) {
+    const int ahead = min(nsl - 1 - s, P::STAGES - 2);
+    if (ahead >= 2) wait_vm<2 * P::DMA>();
+    else if (ahead == 1) wait_vm<P::DMA>();
+    else wait_vm<0>();
+    barrier();
+    if (s + P::STAGES - 1 < nsl) wide_issue(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
+    wide_mma_stage(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn, kh);
+  }
+  barrier();
+}
+
 // Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
 // [128][EPI_LD], multiplied by `scale`: every wave writes its blocks 4 half .. 4 half + 3.  In
 // an 8-wave workgroup each group of 4 waves stages its 128 columns into its own buffer.
