@@ -342,17 +342,39 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
 // (forge_mainloop8.h); the tensors' scale product multiplies the finished sums at staging.
 static_assert(ml8::SMEM <= kSmem2, "fp8 stages fit the shared buffer size");
 
+// The launch covers the nbk 128-column blocks from kb_base on.
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
   int nb, kb;
-  tile_coords((int)(g.N / ml2::BM), (int)(g.K / ml2::BN), nb, kb);
-  const int n0 = nb * ml2::BM, k0 = kb * ml2::BN;
+  tile_coords((int)(g.N / ml2::BM), g.nbk, nb, kb);
+  const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
   ml8::floatx16 acc[4][2];
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
   float* st = reinterpret_cast<float*>(smem);
   tile_epilogue<OPT, WT, ST, 2, false>(g, e, smem, n0, k0, [&](int h) { ml8::stage_acc_half(st, acc, scale, h); });
+}
+
+// fp8 e4m3 inputs on 256 x 256 tiles, one workgroup of 8 waves per CU (forge_mainloop8.h, wide
+// tiles); each 128-column half runs the epilogue from its own staging buffer.
+constexpr int kSmem8W = ml8::W_SMEM > 2 * ml2::EPI_BYTES ? ml8::W_SMEM : 2 * ml2::EPI_BYTES;
+static_assert(kSmem8W <= 160 * 1024, "wide fp8 tiles fit the CU's LDS");
+
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel8w(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem8W];
+  int nb, kb;
+  tile_coords_at((int)blockIdx.x, (int)(g.N / ml2::BM), g.nbk / 2, nb, kb);
+  const int kh = (int)(threadIdx.x >> 8);
+  const int n0 = nb * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
+  ml8::floatx16 acc[4][2];
+  ml8::contract_wide(acc, smem, g, n0, kw0);
+  const float scale = g.dy_scale[0] * g.x_scale[0];
+  unsigned char* mine = smem + kh * ml2::EPI_BYTES;
+  float* st = reinterpret_cast<float*>(mine);
+  tile_epilogue<OPT, WT, ST, 2, false>(g, e, mine, n0, kw0 + kh * ml2::BN,
+                                       [&](int h) { ml8::stage_acc_half(st, acc, scale, h); });
 }
 
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmArgs g, float* dW) {
@@ -607,6 +629,20 @@ static FusedFn fused_for(int w, int s, int opt) {
 }
 
 template <int WT, int ST>
+static FusedFn fused8w_for(int opt) {
+  switch (opt) {
+    case FORGE_OPT_ADAMW: return fused_step_kernel8w<WT, ST, FORGE_OPT_ADAMW>;
+    case FORGE_OPT_NADAM: return fused_step_kernel8w<WT, ST, FORGE_OPT_NADAM>;
+    case FORGE_OPT_RADAM: return fused_step_kernel8w<WT, ST, FORGE_OPT_RADAM>;
+    case FORGE_OPT_LION: return fused_step_kernel8w<WT, ST, FORGE_OPT_LION>;
+    case FORGE_OPT_RMSPROP: return fused_step_kernel8w<WT, ST, FORGE_OPT_RMSPROP>;
+    case FORGE_OPT_ADAGRAD: return fused_step_kernel8w<WT, ST, FORGE_OPT_ADAGRAD>;
+    case FORGE_OPT_SGD: return fused_step_kernel8w<WT, ST, FORGE_OPT_SGD>;
+    case FORGE_OPT_SGD_MOMENTUM: return fused_step_kernel8w<WT, ST, FORGE_OPT_SGD_MOMENTUM>;
+  }
+  return nullptr;
+}
+template <int WT, int ST>
 static FusedFn fused2w_for(int opt) {
   switch (opt) {
     case FORGE_OPT_ADAMW: return fused_step_kernel2w<WT, ST, FORGE_OPT_ADAMW>;
@@ -670,13 +706,34 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
     return (int)hipGetLastError();
   }
   if (use_v8(in_type, g)) {
-    if (w_type == FORGE_W_BF16)
+    FusedFn fw = nullptr;
+    if (w_type == FORGE_W_BF16) {
       fn = s_type == FORGE_S_F32 ? fused8_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused8_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
-    else
+      fw = s_type == FORGE_S_F32 ? fused8w_for<FORGE_W_BF16, FORGE_S_F32>(opt) : fused8w_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+    } else {
       fn = s_type == FORGE_S_F32 ? fused8_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused8_for<FORGE_W_F32, FORGE_S_Q8>(opt);
-    if (!fn) return (int)hipErrorInvalidValue;
-    const unsigned grid8 = (unsigned)((g.N / ml2::BM) * (g.K / ml2::BN));
-    hipLaunchKernelGGL(fn, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g, e);
+      fw = s_type == FORGE_S_F32 ? fused8w_for<FORGE_W_F32, FORGE_S_F32>(opt) : fused8w_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+    }
+    if (!fn || !fw) return (int)hipErrorInvalidValue;
+    GemmArgs g8 = g;
+    g8.kb_base = 0;
+    g8.nbk = (int)(g.K / ml2::BN);
+    // wide tiles first (same rule as for bf16 inputs); the rest on 256 x 128 tiles
+    const int kw = plan_wide(g);
+    if (kw > 0) {
+      GemmArgs gw = g;
+      gw.kb_base = 0;
+      gw.nbk = 2 * kw;
+      const unsigned gridw = (unsigned)((g.N / ml2::BM) * kw);
+      hipLaunchKernelGGL(fw, dim3(gridw), dim3(2 * ml2::THREADS), 0, (hipStream_t)stream, gw, e);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return (int)err;
+      g8.kb_base = 2 * kw;
+      g8.nbk -= 2 * kw;
+      if (g8.nbk == 0) return (int)hipSuccess;
+    }
+    const unsigned grid8 = (unsigned)((g.N / ml2::BM) * g8.nbk);
+    hipLaunchKernelGGL(fn, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g8, e);
     return (int)hipGetLastError();
   }
   if (in_type == FORGE_IN_BF16) fn = fused_for<FORGE_IN_BF16>(w_type, s_type, opt);

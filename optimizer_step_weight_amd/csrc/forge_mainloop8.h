@@ -88,8 +88,10 @@ __device__ __forceinline__ void issue(const Feed& f, unsigned char* stage, int s
 // 32 codes of column c0 + (lane % 32), tokens 32 (lane / 32) .. +31 of the slab: four
 // transpose reads.  Lane i of a 16-lane group addresses token row base + i / 2 and the 8
 // columns c0 + 16 g + 8 (i % 2) .. where g = (lane / 16) % 2 selects the column half.
-template <bool IS_A>
+// WIDE: 256-byte rows with the dY swizzle (the X panel of a wide tile).
+template <bool IS_A, bool WIDE = false>
 __device__ __forceinline__ intx8 frag(const unsigned char* panel, int c0) {
+  constexpr bool A_LIKE = IS_A || WIDE;
   const int lane = threadIdx.x & 63, i = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
   const int col = c0 + 16 * g + 8 * (i & 1);  // multiple of 8: byte offset of the piece
   intx8 out;
@@ -97,7 +99,7 @@ __device__ __forceinline__ intx8 frag(const unsigned char* panel, int c0) {
   for (int r = 0; r < 4; ++r) {
     const int row = 32 * h + 8 * r + (i >> 1);
     const int c = col >> 4;
-    const int off = row * (IS_A ? ROW_A : ROW_B) + 16 * (c ^ (IS_A ? swz_a(row) : swz_b(row))) + (col & 15);
+    const int off = row * (A_LIKE ? ROW_A : ROW_B) + 16 * (c ^ (A_LIKE ? swz_a(row) : swz_b(row))) + (col & 15);
     const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(FORGE_LDS(v2i32, panel + off));
     out[2 * r] = x[0];
     out[2 * r + 1] = x[1];
@@ -148,13 +150,97 @@ __device__ __forceinline__ void contract(floatx16 (&acc)[4][2], unsigned char* s
   barrier();
 }
 
+// ------------------------------------------------------------------ wide tiles (256 x 256)
+// One workgroup of 8 waves contracts a 256 x 256 tile: waves 0-3 the columns k0 .. k0 + 127 and
+// waves 4-7 the columns k0 + 128 .. k0 + 255, each with the wave layout above.  Both groups read
+// the same dY slab; the X slab is 64 token rows of 256 bytes, laid out and swizzled like dY.  A
+// slab moves 32 KiB (one third less than two 256 x 128 tiles) and 4 stages fit in 128 KiB.
+// The per-element token order is that of the 256 x 128 path, so the sums are bitwise equal.
+constexpr int W_STAGES = 4, W_PANEL = TK * ROW_A, W_STAGE = 2 * W_PANEL, W_SMEM = W_STAGES * W_STAGE;
+constexpr int W_DMA = 4;  // per wave per slab: 2 of dY, 2 of X
+
+struct WideFeed {
+  u32x4 rA, rB;
+  uint32_t offA[2], offB[2];
+  uint32_t stepA, stepB;
+};
+
+// A 1 KiB DMA covers 4 token rows of 256 bytes; wave w moves rows 8 w .. 8 w + 7 of each panel.
+__device__ __forceinline__ void make_wide_feed(WideFeed& f, const GemmArgs& g, int n0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f.rA = make_rsrc(g.dY, (uint32_t)(g.T * g.N));
+  f.rB = make_rsrc(g.X, (uint32_t)(g.T * g.K));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 4 * (2 * wave + j) + (lane >> 4), p = lane & 15;
+    f.offA[j] = (uint32_t)(r * g.N + n0 + 16 * (p ^ swz_a(r)));
+    f.offB[j] = (uint32_t)(r * g.K + k0 + 16 * (p ^ swz_a(r)));
+  }
+  f.stepA = (uint32_t)(TK * g.N);
+  f.stepB = (uint32_t)(TK * g.K);
+}
+
+__device__ __forceinline__ void wide_issue(const WideFeed& f, unsigned char* stage, int slab) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rA, f.offA[j] + sa, stage + (2 * wave + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(f.rB, f.offB[j] + sb, stage + W_PANEL + (2 * wave + j) * 1024);
+}
+
+__device__ __forceinline__ void wide_mma_stage(floatx16 (&acc)[4][2], const unsigned char* stage, int wm, int wn,
+                                               int kh) {
+  const unsigned char* pa = stage;
+  const unsigned char* pb = stage + W_PANEL;
+  intx8 b[2];
+#pragma unroll
+  for (int bj = 0; bj < 2; ++bj) b[bj] = frag<false, true>(pb, kh * 128 + wn * 64 + 32 * bj);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    const intx8 a = frag<true>(pa, 128 * (bi >> 1) + 64 * wm + 32 * (bi & 1));
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+      acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[bj], acc[bi][bj], 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// acc = this wave's part of the codes' product sum for the 256 x 256 tile at (n0, k0).  Ends
+// with a barrier (LDS free for reuse).
+__device__ __forceinline__ void contract_wide(floatx16 (&acc)[4][2], unsigned char* smem, const GemmArgs& g, int n0,
+                                              int k0) {
+  const int wave = threadIdx.x >> 6, kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+  WideFeed f;
+  make_wide_feed(f, g, n0, k0);
+  const int nsl = (int)((g.T + TK - 1) / TK);
+#pragma unroll
+  for (int s = 0; s < W_STAGES - 1; ++s)
+    if (s < nsl) wide_issue(f, smem + s * W_STAGE, s);
+  for (int s = 0; s < nsl; ++s) {
+    const int ahead = min(nsl - 1 - s, W_STAGES - 2);
+    if (ahead >= 2) wait_vm<2 * W_DMA>();
+    else if (ahead == 1) wait_vm<W_DMA>();
+    else wait_vm<0>();
+    barrier();
+    if (s + W_STAGES - 1 < nsl) wide_issue(f, smem + ((s + W_STAGES - 1) % W_STAGES) * W_STAGE, s + W_STAGES - 1);
+    wide_mma_stage(acc, smem + (s % W_STAGES) * W_STAGE, wm, wn, kh);
+  }
+  barrier();
+}
+
 // Stage rows [half * 128, half * 128 + 128) of the tile's accumulators in LDS as fp32
 // [128][EPI_LD], times `scale`.  A wave's 32-row blocks bi are rows 128 (bi / 2) + 64 wm +
 // 32 (bi % 2) of the tile (two in each half, so each half frees half of every wave's
 // accumulators).  32 x 32 output layout: register v of lane l holds row 8 (v / 4) + 4 (l / 32) +
 // v % 4, column l % 32 of its block.
 __device__ __forceinline__ void stage_acc_half(float* st, const floatx16 (&acc)[4][2], float scale, int half) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {

@@ -6,9 +6,9 @@ runs in the same order on both paths, so the fused step must equal the unfused p
 256 x 128 GEMM to HBM, then the optimizer kernel) bitwise, whatever mix of launches covers the
 weight.  Shapes (on 256 CUs): 4096 x 4096 is 256 wide tiles (one launch); 2048 x 8192 is 8 x 32
 wide tiles; 4096 x 4224 adds one 128-column block, run as 32 half tiles in the second launch.
-T = 8193 and 8200 leave a ragged last slab of tokens.  The full-size workload tests (the
-Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384) check this path against the
-fp64 oracle on sampled rows.
+T = 8193 and 8200 leave a ragged last slab of tokens.  fp8 inputs follow the same rule.  The
+full-size workload tests (the Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384 in
+bf16 and fp8) check this path against the fp64 oracle on sampled rows.
 """
 from __future__ import annotations
 
@@ -62,6 +62,32 @@ def test_wide_fused_equals_unfused_bitwise(lib, shape, opt, w_fmt, state_fmt, Tn
         X, dY = synth.gaussian_case(700 + t, Tn, Nn, Kn, "bf16")
         pa = a.fused(lib, X, dY, opt, h, t, 23, preround=True)
         pb, _ = b.unfused(lib, X, dY, opt, h, t, 23, preround=True)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb), f"pre-rounding weights differ at step {t}"
+        _same(a, b)
+
+
+# fp8 e4m3 inputs (per-tensor scales) take the same wide tiles for T >= 8192; the rest of the
+# columns run on the 256 x 128 fp8 kernel.
+CASES8 = [((4096, 4096), "adamw", "bf16", "f32", 8192), ((4096, 4224), "nadam", "bf16", "int8", 8200),
+          ((4096, 4096), "lion", "f32", "f32", 8193), ((2048, 8192), "sgd", "bf16", "f32", 8192)]
+
+
+@pytest.mark.parametrize("shape,opt,w_fmt,state_fmt,Tn", CASES8,
+                         ids=[f"fp8-{s[0]}x{s[1]}-{o}-{w}-{st}-T{t}" for s, o, w, st, t in CASES8])
+def test_wide_fp8_fused_equals_unfused_bitwise(lib, shape, opt, w_fmt, state_fmt, Tn):
+    Nn, Kn = shape
+    _say("wide fp8 fused vs unfused", Nn, Kn, opt, w_fmt, state_fmt, "T", Tn)
+    rng = np.random.default_rng(75)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(76, Nn, Kn, w_fmt)
+    m, v = _init_states(opt, state_fmt, rng, Nn, Kn)
+    a = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+    b = P.DeviceStep(W, m, v, w_fmt, state_fmt)
+    for t in (1, 2):
+        X, dY = synth.gaussian_case(750 + t, Tn, Nn, Kn, "fp8")
+        pa = a.fused(lib, X, dY, opt, h, t, 29, preround=True)
+        pb, _ = b.unfused(lib, X, dY, opt, h, t, 29, preround=True)
         torch.cuda.synchronize()
         assert torch.equal(pa, pb), f"pre-rounding weights differ at step {t}"
         _same(a, b)
