@@ -6,7 +6,9 @@
 // tile lives in registers and, for the re-layout to 16 consecutive columns per thread, in the
 // workgroup's LDS; it never reaches HBM.  Three contraction paths, chosen per call:
 //   * bf16 inputs: 256 x 128 tiles (two of the method's 128 x 128 tiles) fed by LDS DMA,
-//     with 128 x 128 half tiles balancing the last round of the launch (forge_mainloop2.h);
+//     two workgroups per CU, with 128 x 128 half tiles balancing the last round of the launch
+//     (forge_mainloop2.h); for T >= 8192, 256 x 256 tiles in one 8-wave workgroup per CU
+//     where they fill whole rounds, the remaining columns in a second 256 x 128 launch;
 //   * fp8 e4m3 inputs: the same tiles with 8-bit transpose reads (forge_mainloop8.h);
 //   * fp32 inputs and layers with too few tiles: 128 x 128 tiles staged through registers
 //     (forge_mainloop.h).
@@ -16,8 +18,9 @@
 // the fp32 gradient to HBM, and a separate element-wise kernel reads it back and applies the
 // same update code.
 //
-// dgrad: dX = dY W on the LDS-DMA path, run before the step so that it sees the old weight
-// (Technical Summary section 5, limitations).
+// dgrad: dX = dY W on the LDS-DMA path (256-token x 256-column tiles in one 8-wave workgroup
+// per CU where K % 256 == 0 and they fill the CUs, else 256 x 128), run before the step so
+// that it sees the old weight (Technical Summary section 5, limitations).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
