@@ -21,7 +21,6 @@ Usage: python bench.py [--gpus 1] [--steps 30] [--warmup 20] [--no-cpu] [--no-ex
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,12 +39,9 @@ PMC_FILE = os.path.join(ROOT, "profiles", "fused_adamw_down_proj_T4096_hbm_count
 
 
 def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "optimizer_step_weight_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    """The library's build id for the sources under ROOT (HBM counters are valid only for them)."""
+    from optimizer_step_weight_amd import _build
+    return _build.source_hash(ROOT)
 
 
 def measured_traffic():

@@ -24,10 +24,12 @@
  *     several gradient consumers in one step are excluded.
  *
  * Conventions for every entry point
- *   - Tensors are row-major and contiguous; every data pointer is a device
- *     pointer to memory of the current HIP device, aligned to 16 bytes.  All
- *     buffers are owned by the caller; the library keeps no pointer after a
- *     call returns and holds no mutable global state.
+ *   - Tensors are row-major and contiguous (row stride `ld` equal to `cols`);
+ *     every data pointer is a device pointer to memory of the current HIP
+ *     device, aligned to 16 bytes.  All buffers are owned by the caller; the
+ *     library keeps no pointer to them after a call returns.  Its only global
+ *     state is a per-device cache (whether the device passed the gfx950 check,
+ *     and its compute-unit count), written once per device and never cleared.
  *   - Shapes: X[T, K] layer input, dY[T, N] upstream gradient, W[N, K] weight
  *     (PyTorch nn.Linear layout), dW[N, K], dX[T, K].  N and K must be
  *     multiples of 128; T may be any value >= 0 (a ragged final token slab is
@@ -55,7 +57,7 @@ typedef enum forge_status {
   FORGE_ERR_ARG = 1,    /* null pointer, step < 1, unknown enum, state given/missing for the rule */
   FORGE_ERR_SHAPE = 2,  /* shapes disagree, N or K not a multiple of 128, N*K >= 2^32 */
   FORGE_ERR_DTYPE = 3,  /* unsupported dtype or dtype combination */
-  FORGE_ERR_LAYOUT = 4, /* pointer not 16-byte aligned */
+  FORGE_ERR_LAYOUT = 4, /* pointer not 16-byte aligned, or row stride ld != cols */
   FORGE_ERR_ALIAS = 5,  /* an output buffer overlaps an input or another output */
   FORGE_ERR_DEVICE = 6, /* no device, or the current device is not gfx950 */
   FORGE_ERR_LAUNCH = 7  /* the HIP runtime refused the launch; see forge_last_error() */
@@ -80,12 +82,16 @@ typedef enum forge_opt {
   FORGE_SGD_MOMENTUM = 7  /* state m (momentum buffer) */
 } forge_opt;
 
-/* A 2-D tensor descriptor.  `scale` is a device pointer (see forge_dtype) or NULL. */
+/* A 2-D tensor descriptor.  `ld` is the row stride in elements; every entry point requires
+ * ld == cols (contiguous rows) and returns FORGE_ERR_LAYOUT otherwise.  `scale` is a device
+ * pointer (see forge_dtype) or NULL; the library cannot see its allocation size, so the
+ * caller must provide the element count the dtype names. */
 typedef struct forge_tensor {
   void* data;
   int32_t dtype; /* forge_dtype */
   int64_t rows;
   int64_t cols;
+  int64_t ld;
   void* scale;
 } forge_tensor;
 
@@ -176,6 +182,10 @@ forge_status forge_optimizer_step(const forge_tensor* dW, forge_tensor* W, forge
  */
 forge_status forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, float* out,
                                 int32_t n_out);
+
+/* Hash of the sources the library was built from (16 hex digits); a caller can compare it
+ * with the sources it ships to make sure a stale binary is never used. */
+const char* forge_build_id(void);
 
 const char* forge_status_string(forge_status s);
 const char* forge_last_error(void); /* text of this thread's last error ("" if none) */

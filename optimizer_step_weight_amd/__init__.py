@@ -3,11 +3,14 @@
 Argument marshalling only: every step of the computation runs in the library's HIP
 kernels.  Tensors are PyTorch device tensors (PyTorch provides device memory and the
 stream); they are passed to the C ABI as raw pointers and sizes.  If the library is not
-built, every call raises: there is no fallback path.
+built, or was built from other sources than the ones beside it, every call raises: there is
+no fallback path.  Tensors must be CUDA tensors on the current device; scale tensors must be
+fp32 with the element count their tensor's format names (the library cannot see allocation
+sizes, so a short buffer would be read out of bounds).
 
 Entry points (same names as the C ABI in include/forge.h, without the ``forge_`` prefix):
     wgrad_step, dgrad, linear_backward_step, wgrad_gemm, optimizer_step,
-    step_scalars, device_check, version, status_string, last_error
+    step_scalars, device_check, version, build_id, status_string, last_error
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ class ForgeError(RuntimeError):
 
 class Tensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("scale", ctypes.c_void_p)]
+                ("cols", ctypes.c_int64), ("ld", ctypes.c_int64), ("scale", ctypes.c_void_p)]
 
 
 class Hyper(ctypes.Structure):
@@ -69,10 +72,16 @@ def _lib():
         L.forge_status_string.restype = ctypes.c_char_p
         L.forge_last_error.restype = ctypes.c_char_p
         L.forge_version.restype = i32
+        L.forge_build_id.restype = ctypes.c_char_p
         L.forge_device_check.argtypes = [i32]
         for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_wgrad_gemm",
                   "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
             getattr(L, f).restype = st
+        from . import _build
+        built, want = L.forge_build_id().decode(), _build.source_hash()
+        if built != want:
+            raise ImportError(f"{LIB_PATH} was built from other sources (build id {built}, sources {want}); "
+                              "rebuild it with __graft_entry__.build()")
         _lib_handle = L
     return _lib_handle
 
@@ -97,12 +106,40 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _on_device(t, what: str):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor (got a {t.device} tensor)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _scale_count(code: int, rows: int, cols: int) -> Optional[int]:
+    """Element count of the scale buffer a format needs (None: the format has no scale)."""
+    if code == FP8_E4M3:
+        return 1
+    if code in (I8_B64, U8_B64):
+        return rows * cols // 64
+    return None
+
+
 def _tensor(t, scale=None) -> Optional[Tensor]:
+    import torch
     if t is None:
         return None
-    if t.dim() != 2 or not t.is_contiguous():
-        raise ValueError("tensors must be 2-D and contiguous")
-    return Tensor(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1],
+    if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+        raise ValueError("tensors must be 2-D with unit column stride")
+    code = _dtype_code(t)
+    want = _scale_count(code, t.shape[0], t.shape[1])
+    if scale is not None:
+        if want is None:
+            raise ValueError(f"a {t.dtype} tensor takes no scale")
+        if scale.dtype != torch.float32 or not scale.is_contiguous() or scale.numel() != want:
+            raise ValueError(f"the scale of a {t.dtype} [{t.shape[0]}, {t.shape[1]}] tensor must be a contiguous "
+                             f"float32 tensor of {want} elements (got {scale.dtype}, {scale.numel()})")
+        _on_device(scale, "scale")
+    _on_device(t, "tensor")
+    return Tensor(t.data_ptr(), code, t.shape[0], t.shape[1], t.stride(0) if t.numel() > 0 else t.shape[1],
                   None if scale is None else scale.data_ptr())
 
 
@@ -128,9 +165,15 @@ def _stream(stream) -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _opts(w_preround_out, sr):
+def _opts(w_preround_out, sr, W):
     if w_preround_out is None and sr:
         return None
+    if w_preround_out is not None:
+        import torch
+        _on_device(w_preround_out, "w_preround_out")
+        if (w_preround_out.dtype != torch.float32 or not w_preround_out.is_contiguous()
+                or w_preround_out.numel() != W.numel()):
+            raise ValueError("w_preround_out must be a contiguous float32 tensor with one element per weight")
     return StepOpts(None if w_preround_out is None else w_preround_out.data_ptr(), 1 if sr else 0)
 
 
@@ -138,7 +181,7 @@ def wgrad_step(X, dY, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, 
                x_scale=None, dy_scale=None, m_scale=None, v_scale=None, w_preround_out=None, sr=True,
                stream=None):
     """Fused step: W, m, v updated in place from g = dY^T X (forge_wgrad_step)."""
-    o = _opts(w_preround_out, sr)
+    o = _opts(w_preround_out, sr, W)
     _check(_lib().forge_wgrad_step(_ref(_tensor(X, x_scale)), _ref(_tensor(dY, dy_scale)), _ref(_tensor(W)),
                                    _ref(_tensor(m, m_scale)), _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)),
                                    _opt(opt), int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
@@ -152,7 +195,7 @@ def dgrad(dY, W, dX, *, stream=None):
 def linear_backward_step(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
                          m_scale=None, v_scale=None, w_preround_out=None, sr=True, stream=None):
     """dgrad then the fused step, in that order (forge_linear_backward_step)."""
-    o = _opts(w_preround_out, sr)
+    o = _opts(w_preround_out, sr, W)
     _check(_lib().forge_linear_backward_step(
         _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale)),
         _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
@@ -168,7 +211,7 @@ def wgrad_gemm(X, dY, dW, *, x_scale=None, dy_scale=None, stream=None):
 def optimizer_step(dW, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int, m_scale=None,
                    v_scale=None, w_preround_out=None, sr=True, stream=None):
     """Unfused phase 2: the rule applied to a materialised gradient (forge_optimizer_step)."""
-    o = _opts(w_preround_out, sr)
+    o = _opts(w_preround_out, sr, W)
     _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale)),
                                        _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
                                        int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
@@ -189,6 +232,10 @@ def version() -> int:
     return int(_lib().forge_version())
 
 
+def build_id() -> str:
+    return _lib().forge_build_id().decode()
+
+
 def status_string(status: int) -> str:
     return _lib().forge_status_string(int(status)).decode()
 
@@ -206,5 +253,6 @@ forge_optimizer_step = optimizer_step
 forge_step_scalars = step_scalars
 forge_device_check = device_check
 forge_version = version
+forge_build_id = build_id
 forge_status_string = status_string
 forge_last_error = last_error

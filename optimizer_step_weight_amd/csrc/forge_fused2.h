@@ -1,0 +1,88 @@
+// forge_fused2.h -- the fused step for bf16 inputs on the LDS-DMA path (forge_mainloop2.h):
+// 256 x 128 tiles, two workgroups per CU, with 128 x 128 half tiles balancing the last round of
+// a launch, and 256 x 256 tiles in one 8-wave workgroup per CU for long token counts.
+// FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism".
+//
+// Instantiated per moment format in forge_fused2_f32.hip and forge_fused2_q8.hip.
+#pragma once
+
+#include "forge_epilogue.h"
+
+namespace forge {
+
+// Full 256 x 128 tile: contraction, then the epilogue over its two 128-row halves.
+template <int WT, int ST, int OPT>
+__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
+  int nb, kb;
+  tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
+  const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+  float* st = reinterpret_cast<float*>(smem);
+  tile_epilogue<OPT, WT, ST, 2, true>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
+}
+
+// Half 128 x 128 tile hb of the blocks [kb_split, nbk): all 128 rows staged at once.
+template <int WT, int ST, int OPT>
+__device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
+  int nb, kb;
+  tile_coords_at(hb, (int)(g.N / ml2::BM_HALF), g.nbk - g.kb_split, nb, kb);
+  const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
+  ml2::floatx4 acc[4][4];
+  ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
+  float* st = reinterpret_cast<float*>(smem);
+  tile_epilogue<OPT, WT, ST, 1, true>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
+}
+
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
+  const int b = (int)blockIdx.x;
+  if (b < g.nfull) fused_full_tile<WT, ST, OPT>(g, e, smem, b);
+  else fused_half_tile<WT, ST, OPT>(g, e, smem, b - g.nfull);
+}
+
+// bf16 inputs, 256 x 256 tiles, one workgroup of 8 waves per CU (forge_mainloop2.h, wide
+// tiles): both 128-column halves share the dY panel and 4 slabs fit in LDS.  The epilogue is
+// the 256 x 128 tile's, run by each half: threads 0-255 update columns k0 .. k0 + 127 and
+// threads 256-511 columns k0 + 128 .. k0 + 255, each staging through its own LDS buffer.  The
+// launch covers the nbk / 2 wide column blocks from kb_base / 2 on.
+constexpr int kSmemW = ml2::WidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::WidePipe::SMEM : 2 * ml2::EPI_BYTES;
+static_assert(kSmemW <= 160 * 1024, "wide tiles fit the CU's LDS");
+
+template <int WT, int ST, int OPT>
+__global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel2w(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemW];
+  int nb, kb;
+  tile_coords_at((int)blockIdx.x, (int)(g.N / ml2::BM), g.nbk / 2, nb, kb);
+  const int kh = (int)(threadIdx.x >> 8);
+  const int n0 = nb * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
+  ml2::floatx4 acc[8][4];
+  ml2::contract_wide(acc, smem, g, n0, kw0);
+  unsigned char* mine = smem + kh * ml2::EPI_BYTES;
+  float* st = reinterpret_cast<float*>(mine);
+  tile_epilogue<OPT, WT, ST, 2, true>(g, e, mine, n0, kw0 + kh * ml2::BN,
+                                      [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
+}
+
+template <int ST>
+FusedFn select_fused2(int wide, int w_type, int opt) {
+  if (w_type == FORGE_W_BF16) {
+    switch (opt) {
+#define FORGE_CASE(O) \
+  case O: return wide ? fused_step_kernel2w<FORGE_W_BF16, ST, O> : fused_step_kernel2<FORGE_W_BF16, ST, O>;
+      FORGE_FOR_EACH_OPT(FORGE_CASE)
+#undef FORGE_CASE
+    }
+  } else {
+    switch (opt) {
+#define FORGE_CASE(O) \
+  case O: return wide ? fused_step_kernel2w<FORGE_W_F32, ST, O> : fused_step_kernel2<FORGE_W_F32, ST, O>;
+      FORGE_FOR_EACH_OPT(FORGE_CASE)
+#undef FORGE_CASE
+    }
+  }
+  return nullptr;
+}
+
+}  // namespace forge

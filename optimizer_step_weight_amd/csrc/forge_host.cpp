@@ -73,6 +73,9 @@ forge_status check_tensor(const forge_tensor* t, const char* name) {
   if (dtype_size(t->dtype) == 0) return fail(FORGE_ERR_DTYPE, "%s has unknown dtype %d", name, (int)t->dtype);
   if (t->rows * t->cols > 0 && !t->data) return fail(FORGE_ERR_ARG, "%s->data is NULL", name);
   if (!aligned16(t->data)) return fail(FORGE_ERR_LAYOUT, "%s->data is not 16-byte aligned", name);
+  if (t->rows > 0 && t->ld != t->cols)
+    return fail(FORGE_ERR_LAYOUT, "%s has row stride %lld, expected %lld (contiguous rows)", name, (long long)t->ld,
+                (long long)t->cols);
   return FORGE_OK;
 }
 
@@ -420,6 +423,11 @@ const char* forge_status_string(forge_status s) {
 const char* forge_last_error(void) { return g_last_error.c_str(); }
 
 int32_t forge_version(void) { return FORGE_VERSION; }
+
+#ifndef FORGE_BUILD_ID
+#define FORGE_BUILD_ID "unknown"
+#endif
+const char* forge_build_id(void) { return FORGE_BUILD_ID; }
 
 forge_status forge_device_check(int32_t device) {
   int count = 0;

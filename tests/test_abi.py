@@ -39,11 +39,18 @@ def test_exports_every_declared_symbol(forge):
     assert forge.status_string(0) == "ok" and forge.status_string(5) == "overlapping buffers"
 
 
+def test_build_id_matches_the_sources(forge):
+    """The library embeds the hash of the sources it was built from; the binding refuses a stale one."""
+    from optimizer_step_weight_amd import _build
+    assert forge.build_id() == _build.source_hash()
+    assert re.fullmatch(r"[0-9a-f]{16}", forge.build_id())
+
+
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
-def _t(f, rows, cols, dtype, off=0, scale=None):
-    return f.Tensor(FAKE + off, dtype, rows, cols, scale)
+def _t(f, rows, cols, dtype, off=0, scale=None, ld=None):
+    return f.Tensor(FAKE + off, dtype, rows, cols, cols if ld is None else ld, scale)
 
 
 def _call_step(f, X, dY, W, m, v, opt=0, step=1, hyper=None, opts=None):
@@ -78,6 +85,8 @@ def test_validation_codes(forge):
         ((X(), dY(), W(), m(dt=f.U8_B64), v()), {}, 3),                      # m must be signed
         ((X(), dY(), W(), _t(f, N, K, f.I8_B64, 3 * GB, scale=FAKE + 5 * GB), v()), {}, 3),  # m int8, v fp32
         ((_t(f, T, K, f.BF16, 8), dY(), W(), m(), v()), {}, 4),              # misaligned
+        ((_t(f, T, K, f.BF16, ld=2 * K), dY(), W(), m(), v()), {}, 4),       # X rows not contiguous
+        ((X(), dY(), W(), m(), _t(f, N, K, f.F32, 4 * GB, ld=K + 4)), {}, 4),  # v rows not contiguous
         ((X(), dY(), W(off=0), m(), v()), {}, 5),                            # W aliases X
         ((X(), dY(), W(), m(off=2 * GB + 4096 * 16), v()), {}, 5),         # m overlaps W
         ((_t(f, T, K, f.FP8_E4M3), _t(f, T, N, f.FP8_E4M3, GB), W(), m(), v()), {}, 1),  # fp8 without scales
@@ -101,6 +110,7 @@ def test_dgrad_and_unfused_validation(forge):
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 256, f.BF16, 2 * GB)), None) == 2
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 384, f.F32, 2 * GB)), None) == 3
     assert L.forge_dgrad(r(dY), r(W), r(_t(f, 100, 384, f.BF16, 0)), None) == 5
+    assert L.forge_dgrad(r(dY), r(_t(f, 256, 384, f.BF16, GB, ld=512)), r(dX), None) == 4
     # 32-bit offsets: W of 2^31 elements, or dY that reaches 2^31 elements with one tile of tokens
     assert L.forge_dgrad(r(_t(f, 100, 131072, f.BF16)), r(_t(f, 131072, 16384, f.BF16, GB)),
                          r(_t(f, 100, 16384, f.BF16, 2 * GB)), None) == 2
@@ -138,3 +148,28 @@ def test_host_scalars_match_oracle(forge, opt, t):
         assert s["b2"] == f32(p["alpha"]) and s["omb2"] == f32(1 - p["alpha"])
     if opt == "sgd_momentum":
         assert s["c1"] == f32(p["momentum"])
+
+
+def test_binding_rejects_host_tensors_and_short_scales(forge):
+    """The binding refuses what the C ABI cannot see: host memory and scale buffers of the wrong size."""
+    import torch
+    h = synth.default_hyper("adamw")
+    X = torch.zeros((64, 256), dtype=torch.bfloat16)
+    dY = torch.zeros((64, 256), dtype=torch.bfloat16)
+    W = torch.zeros((256, 256), dtype=torch.bfloat16)
+    m, v = torch.zeros((256, 256)), torch.zeros((256, 256))
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        forge.wgrad_step(X, dY, W, m, v, opt="adamw", hyper=h, step=1, seed=1)
+    m8, v8 = torch.zeros((256, 256), dtype=torch.int8), torch.zeros((256, 256), dtype=torch.uint8)
+    short = torch.zeros(256 * 256 // 64 - 1)
+    # each tensor's scale is checked before its device (so the checks are visible without a GPU)
+    with pytest.raises(ValueError, match="1023"):
+        forge._tensor(m8, short)
+    with pytest.raises(ValueError, match="float32"):
+        forge._tensor(v8, torch.zeros(1024, dtype=torch.float16))
+    with pytest.raises(ValueError, match="takes no scale"):
+        forge._tensor(m, torch.zeros(1024))
+    with pytest.raises(ValueError, match="1 elements"):
+        forge._tensor(torch.zeros((64, 256), dtype=torch.float8_e4m3fn), torch.zeros(2))
+    with pytest.raises(ValueError, match="unit column stride"):
+        forge.dgrad(dY.t(), W, torch.zeros((256, 256), dtype=torch.bfloat16))

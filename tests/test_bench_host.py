@@ -33,21 +33,27 @@ def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch
 
 
 def test_source_hash_covers_every_kernel_source(tmp_path, monkeypatch):
-    """A change to any file under csrc/ changes the hash (so stale counters are dropped)."""
-    csrc = tmp_path / "optimizer_step_weight_amd" / "csrc"
-    csrc.mkdir(parents=True)
-    src = os.path.join(ROOT, "optimizer_step_weight_amd", "csrc")
-    for name in sorted(os.listdir(src)):
-        with open(os.path.join(src, name), "rb") as fh:
-            (csrc / name).write_bytes(fh.read())
+    """A change to any library source (csrc/, include/) changes the hash, so stale counters are
+    dropped and a stale library is refused."""
+    dirs = []
+    for rel in (("optimizer_step_weight_amd", "csrc"), ("include",)):
+        dst = tmp_path.joinpath(*rel)
+        dst.mkdir(parents=True)
+        src = os.path.join(ROOT, *rel)
+        for name in sorted(os.listdir(src)):
+            if name.endswith((".h", ".hip", ".cpp")):
+                with open(os.path.join(src, name), "rb") as fh:
+                    (dst / name).write_bytes(fh.read())
+        dirs.append(dst)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0 = bench.source_hash()
-    for name in sorted(os.listdir(csrc)):
-        p = csrc / name
-        old = p.read_bytes()
-        p.write_bytes(old + b"\n")
-        assert bench.source_hash() != h0, name
-        p.write_bytes(old)
+    for d in dirs:
+        for name in sorted(os.listdir(d)):
+            p = d / name
+            old = p.read_bytes()
+            p.write_bytes(old + b"\n")
+            assert bench.source_hash() != h0, name
+            p.write_bytes(old)
     assert bench.source_hash() == h0
 
 
