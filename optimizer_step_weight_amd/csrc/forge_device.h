@@ -141,6 +141,47 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
+// ------------------------------------------------------------------ int8 block-64 requantisation
+// The new values x[0..C) of this lane, part of a 64-element block spread over LANES lanes
+// (lane ^ 1, 2, ... < LANES; all of them active).  Returns the block scale and the codes:
+//  * scale = absmax of the block; code = nearest-even of x * levels / scale, levels 127
+//    (signed, codes -127..127) or 255 (unsigned, codes 0..255);
+//  * an unsigned (second-moment) value above zero never stores code 0, its code is at least 1:
+//    otherwise about one value in eleven of a Gaussian block would store 0, and the next step's
+//    denominator would lose that element's history while its first moment keeps it;
+//  * a block of zeros stores zero codes with scale 0; a block holding a NaN or an infinity
+//    stores zero codes and a NaN scale, so it dequantises to NaN and stays visible.
+template <bool SIGNED, int C, int LANES>
+__device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&code)[C]) {
+  float amax = 0.0f;
+  int bad = 0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const float a = fabsf(x[j]);
+    bad |= !(a <= 3.40282347e38f);
+    amax = fmaxf(amax, a);
+  }
+#pragma unroll
+  for (int o = 1; o < LANES; o <<= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    bad |= __shfl_xor(bad, o);
+  }
+  const float inv = (!bad && amax > 0.0f) ? (SIGNED ? 127.0f : 255.0f) / amax : 0.0f;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const float xj = bad ? 0.0f : x[j];
+    float q = __builtin_rintf(xj * inv);
+    if constexpr (SIGNED) {
+      q = fminf(fmaxf(q, -127.0f), 127.0f);
+      code[j] = (uint32_t)(int32_t)q & 0xFFu;
+    } else {
+      q = fminf(fmaxf(q, (xj > 0.0f && inv > 0.0f) ? 1.0f : 0.0f), 255.0f);
+      code[j] = (uint32_t)q;
+    }
+  }
+  return bad ? __builtin_nanf("") : amax;
+}
+
 // ------------------------------------------------------------------ one 16-element segment
 // The stored state of 16 consecutive elements, as loaded from memory (raw words).
 struct SegIn {
@@ -300,26 +341,14 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
         st16(mp + 4 * q, a);
       }
     } else {
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(m[j]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      uint32_t code[16];
+      const float scale = quant_block64<true, 16, 4>(m, code);
       u32x4 a;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float qv = __builtin_rintf(m[4 * q + c] * inv);
-          qv = fminf(fmaxf(qv, -127.0f), 127.0f);
-          word |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * c);
-        }
-        a[q] = word;
-      }
+      for (int q = 0; q < 4; ++q)
+        a[q] = code[4 * q] | (code[4 * q + 1] << 8) | (code[4 * q + 2] << 16) | (code[4 * q + 3] << 24);
       st16(static_cast<int8_t*>(e.m) + i0, a);
-      if (leader) e.m_scale[i0 >> 6] = amax;
+      if (leader) e.m_scale[i0 >> 6] = scale;
     }
   }
   if constexpr (HV) {
@@ -333,26 +362,14 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
         st16(vp + 4 * q, a);
       }
     } else {
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      const float inv = amax > 0.0f ? 255.0f / amax : 0.0f;
+      uint32_t code[16];
+      const float scale = quant_block64<false, 16, 4>(v, code);
       u32x4 a;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float qv = __builtin_rintf(v[4 * q + c] * inv);
-          qv = fminf(fmaxf(qv, 0.0f), 255.0f);
-          word |= ((uint32_t)qv & 0xFFu) << (8 * c);
-        }
-        a[q] = word;
-      }
+      for (int q = 0; q < 4; ++q)
+        a[q] = code[4 * q] | (code[4 * q + 1] << 8) | (code[4 * q + 2] << 16) | (code[4 * q + 3] << 24);
       st16(static_cast<uint8_t*>(e.v) + i0, a);
-      if (leader) e.v_scale[i0 >> 6] = amax;
+      if (leader) e.v_scale[i0 >> 6] = scale;
     }
   }
 }
@@ -516,21 +533,10 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(m[c]);
       st16(static_cast<float*>(e.m) + i0, a);
     } else {
-      float amax = fmaxf(fmaxf(fabsf(m[0]), fabsf(m[1])), fmaxf(fabsf(m[2]), fabsf(m[3])));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
-      amax = fmaxf(amax, __shfl_xor(amax, 8));
-      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-      uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float qv = __builtin_rintf(m[c] * inv);
-        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
-        word |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * c);
-      }
-      st4(static_cast<int8_t*>(e.m) + i0, word);
-      if (leader) e.m_scale[i0 >> 6] = amax;
+      uint32_t code[4];
+      const float scale = quant_block64<true, 4, 16>(m, code);
+      st4(static_cast<int8_t*>(e.m) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
+      if (leader) e.m_scale[i0 >> 6] = scale;
     }
   }
   if constexpr (HV) {
@@ -540,21 +546,10 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[c]);
       st16(static_cast<float*>(e.v) + i0, a);
     } else {
-      float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
-      amax = fmaxf(amax, __shfl_xor(amax, 8));
-      const float inv = amax > 0.0f ? 255.0f / amax : 0.0f;
-      uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float qv = __builtin_rintf(v[c] * inv);
-        qv = fminf(fmaxf(qv, 0.0f), 255.0f);
-        word |= ((uint32_t)qv & 0xFFu) << (8 * c);
-      }
-      st4(static_cast<uint8_t*>(e.v) + i0, word);
-      if (leader) e.v_scale[i0 >> 6] = amax;
+      uint32_t code[4];
+      const float scale = quant_block64<false, 4, 16>(v, code);
+      st4(static_cast<uint8_t*>(e.v) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
+      if (leader) e.v_scale[i0 >> 6] = scale;
     }
   }
 }

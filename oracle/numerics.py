@@ -12,13 +12,20 @@
   magnitude is 448.
 * Block-64 int8 optimizer moments (same section "Precision and Fidelity":
   int8 optimizer states use blocks of 64 elements instead of 2048).  Reading
-  used here: blocks are 64 consecutive elements of the row-major tensor, the
-  block scale is the fp32 absmax of the new fp32 values, signed moments use
-  codes -127..127 and non-negative moments use 0..255, code = round-half-even
-  of value * levels / scale, dequantised value = code * scale / levels, and a
-  block with scale 0 stores all-zero codes.  Where a floating-point value
-  decides an integer code, the decision is taken in fp32, the kernel's
-  precision: scale, reciprocal and product are each rounded to fp32.
+  used here: blocks are 64 consecutive elements of the row-major tensor; the
+  stored block scale s is the block's absmax rounded to fp32; signed moments
+  use codes -127..127 and non-negative moments use 0..255; code =
+  round-half-even of value * levels / s, taken in float64 from the new value;
+  dequantised value = code * s / levels.  Two readings the pages leave open:
+  - a non-negative (second) moment that is not zero never stores code 0: its
+    code is at least 1.  Plain rounding would store about one value in eleven
+    of a Gaussian block as 0, the next step's denominator would then lose that
+    element's history while its first moment keeps it, and single updates
+    would grow by orders of magnitude; the pages claim full-precision
+    fidelity for the int8 states (section 3), which rules that out;
+  - a block with scale 0 stores all-zero codes; a block holding a NaN or an
+    infinity stores all-zero codes and a NaN scale, so it dequantises to NaN
+    and a non-finite moment stays visible.
 """
 from __future__ import annotations
 
@@ -128,19 +135,21 @@ def levels(signed: bool) -> int:
 
 def quantize_block64(x64: np.ndarray, signed: bool):
     """Quantise a [rows, cols] moment (cols % 64 == 0) -> (codes, fp32 scales[rows, cols/64])."""
-    x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
-    rows, cols = x32.shape
+    x = np.asarray(x64, dtype=np.float64)
+    rows, cols = x.shape
     assert cols % BLOCK == 0
-    xb = x32.reshape(rows, cols // BLOCK, BLOCK)
-    s = np.max(np.abs(xb), axis=2).astype(np.float32)
+    xb = x.reshape(rows, cols // BLOCK, BLOCK)
+    finite = np.isfinite(xb).all(axis=2)
+    with np.errstate(invalid="ignore", over="ignore"):
+        s = np.where(finite, np.max(np.abs(np.where(np.isfinite(xb), xb, 0.0)), axis=2), np.nan).astype(np.float32)
     lv = levels(signed)
-    with np.errstate(divide="ignore"):
-        inv = np.where(s > 0, (np.float64(lv) / s.astype(np.float64)), 0.0).astype(np.float32)
-    prod = (xb.astype(np.float64) * inv[..., None].astype(np.float64)).astype(np.float32)
-    q = np.rint(prod)
+    use = finite & (s > 0)
+    s64 = np.where(use, s.astype(np.float64), 1.0)[..., None]
+    q = np.where(use[..., None], np.rint(np.where(np.isfinite(xb), xb, 0.0) * lv / s64), 0.0)
     if signed:
         codes = np.clip(q, -127, 127).astype(np.int8)
     else:
+        q = np.where(use[..., None] & (xb > 0), np.maximum(q, 1.0), q)
         codes = np.clip(q, 0, 255).astype(np.uint8)
     return codes.reshape(rows, cols), s
 
