@@ -176,6 +176,23 @@ class Timer:
         return per
 
 
+def clock_during(forge, fn, reps, seconds):
+    """Average shader clock (MHz) while `fn` runs `reps` times back to back on the current
+    stream: a one-wave sampler on a second stream (default priority) spans the first `seconds`
+    of the run, measuring shader-clock cycles against the constant-rate real-time counter."""
+    import torch
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    forge.clock_sample(seconds, out, stream=side.cuda_stream)
+    for i in range(reps):
+        fn(i)
+    torch.cuda.synchronize()
+    cycles, ticks = (int(x) for x in out.tolist())
+    hz = forge.realtime_hz()
+    return round(cycles / (ticks / hz) / 1e6, 1) if ticks > 0 and hz > 0 else None
+
+
 def workload_timings(forge, timer, reps):
     """The other workloads' steps on device-generated Gaussian inputs of the same shapes and scales:
     the 7-linear Llama-3.1-8B block (dgrad then the fused step per layer, T = 8192), the Qwen3-14B
@@ -370,8 +387,12 @@ def main():
     ms, per_step = timer.warm(step, a.steps)            # the timed region: `steps` fused steps back to back
     fused_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
     tflops = tflops_of(ms)
-    print(f"[bench] fused step {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    extra = {"fused_us_warm": pctl(per_step), "fused_peak_extra_bytes": int(fused_peak_extra)}
+    # the shader clock over the same back-to-back launches, measured right after the timed region
+    clock = clock_during(forge, step, a.steps, 0.6 * a.steps * ms * 1e-3)
+    print(f"[bench] fused step {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s, shader clock {clock} MHz", file=sys.stderr,
+          flush=True)
+    extra = {"fused_us_warm": pctl(per_step), "fused_peak_extra_bytes": int(fused_peak_extra),
+             "shader_clock_mhz_fused": clock}
     if not a.no_extra:
         extra["fused_us_cold"] = pctl(timer.cold(step, 10))
         # unfused two-phase baseline: dW GEMM to HBM, then the optimizer kernel
@@ -393,6 +414,7 @@ def main():
         for i in range(3):
             unfused(i)
         unf_ms, unf_per = timer.warm(unfused, a.steps)
+        extra["shader_clock_mhz_unfused"] = clock_during(forge, unfused, a.steps, 0.6 * a.steps * unf_ms * 1e-3)
         unf_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
         gemm_ms, _ = timer.warm(gemm, a.steps)
         opt_ms, _ = timer.warm(opt_step, a.steps)

@@ -73,6 +73,9 @@ def _lib():
         L.forge_last_error.restype = ctypes.c_char_p
         L.forge_version.restype = i32
         L.forge_build_id.restype = ctypes.c_char_p
+        L.forge_clock_sample.argtypes = [ctypes.c_double, vp, vp]
+        L.forge_clock_sample.restype = st
+        L.forge_realtime_hz.restype = ctypes.c_double
         L.forge_device_check.argtypes = [i32]
         for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_wgrad_gemm",
                   "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
@@ -234,6 +237,19 @@ def version() -> int:
 
 def build_id() -> str:
     return _lib().forge_build_id().decode()
+
+
+def clock_sample(seconds: float, out, *, stream=None) -> None:
+    """Measurement helper (include/forge_measure.h): one wave on `stream` writes the shader-clock
+    cycles and real-time ticks of a `seconds`-long interval to `out` (2 x int64, device)."""
+    _on_device(out, "out")
+    if out.numel() < 2 or out.element_size() != 8 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 64-bit tensor of at least 2 elements")
+    _check(_lib().forge_clock_sample(float(seconds), out.data_ptr(), _stream(stream)))
+
+
+def realtime_hz() -> float:
+    return float(_lib().forge_realtime_hz())
 
 
 def status_string(status: int) -> str:

@@ -286,6 +286,50 @@ def int8_envelope_close(gpu, lo, hi, signed: bool, what: str):
                              f"want [{qlo.flat[i]:.3f}, {qhi.flat[i]:.3f}] +- 1")
 
 
+def init_states(opt, state_fmt, rng, N, K):
+    """Non-trivial previous moments in the rule's domain (v >= 0)."""
+    m, v = wgrad.init_states(opt, N, K, state_fmt)
+    mm = rng.standard_normal((N, K)) * 2e-3
+    vv = np.abs(rng.standard_normal((N, K))) * 1e-5
+    if opt == "adagrad":
+        vv = vv * 10
+    if state_fmt == "f32":
+        m = None if m is None else mm.astype(np.float32)
+        v = None if v is None else vv.astype(np.float32)
+    else:
+        m = None if m is None else numerics.quantize_block64(mm, True)
+        v = None if v is None else numerics.quantize_block64(vv, False)
+    return m, v
+
+
+def compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, W_old, env=None, tag="", lion=None):
+    """env = (lo, hi, moment ranges) from parity.envelope for inputs whose sums are not exact.
+
+    lion = (hyper, step, m_old, v_old) for Lion with exact sums: sign(c) of c = b1 m + (1 - b1) g
+    is still ambiguous where c is within fp32 rounding of 0, so the range with tau = 0 is used.
+    """
+    if env is None and lion is not None:
+        h, t, m_old, v_old = lion
+        env = envelope("lion", h, t, ref["g"], np.zeros_like(ref["g"]), W_old, m_old, v_old, w_fmt, state_fmt)
+    lo, hi, mom = env if env is not None else (None, None, {})
+    slack = arith_slack(W_old, w_fmt, ref["W64"])
+    weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W", slack=slack)
+    if pre is not None:
+        preround_close(pre, ref["W64"] if lo is None else lo, ref["W64"] if hi is None else hi, what=f"{tag} W32")
+    state_close(got_m, ref["m"], ref["m64"], state_fmt, f"{tag} m", *mom.get("m", (None, None)))
+    state_close(got_v, ref["v"], ref["v64"], state_fmt, f"{tag} v", *mom.get("v", (None, None)))
+
+
+def norm_gate(gpu: np.ndarray, ref64: np.ndarray, what: str, tol: float = 1e-5) -> float:
+    """Tensor-wide gate: ||gpu - ref|| / ||ref|| <= tol (returns the ratio)."""
+    g = np.asarray(gpu, np.float64)
+    num = float(np.linalg.norm((g - ref64).ravel()))
+    den = float(np.linalg.norm(np.asarray(ref64, np.float64).ravel()))
+    r = num / den if den > 0 else num
+    assert r <= tol, f"{what}: ||gpu - ref|| / ||ref|| = {r:.3e} > {tol:.0e}"
+    return r
+
+
 def grad_bound_rows(X64: np.ndarray, dY64_rows: np.ndarray, g: np.ndarray, fp8: bool) -> np.ndarray:
     """grad_bound for the rows of W whose dY columns are given (decoded inputs)."""
     T = X64.shape[0]

@@ -1,7 +1,9 @@
 """The autograd layer (optimizer_step_weight_amd.autograd.FusedLinear) on the GPU.
 
-* one backward equals the library's own calls: dX from the old weight, W / m / v from the
-  fused step on the same X and dY (the wrapper passes the right tensors in the right order);
+* one backward against the CPU oracle: dX within the summation bound of dY W with the old
+  weight (plus one bf16 ULP), W / m / v within the parity bar of the oracle's fused step on the
+  same X and dY (so the wrapper passes the right tensors, in the right order, with the right
+  step count);
 * the weight is updated even when the layer's input needs no gradient;
 * a small synthetic training loop (a two-layer ReLU network fitting a random teacher network)
   with FusedLinear layers tracks the same network trained in fp32 with torch.optim.AdamW
@@ -30,29 +32,32 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def test_one_backward_equals_library_calls(lib):
+def test_one_backward_matches_the_oracle(lib):
+    import synth
+    from oracle import numerics, wgrad
     from optimizer_step_weight_amd.autograd import FusedLinear
-    _say("autograd one step")
+    from tests import parity as P
+    _say("autograd one step against the oracle")
     torch.manual_seed(0)
-    hyper = {"lr": 1e-3, "weight_decay": 0.01}
+    hyper = synth.Hyper(lr=1e-3, weight_decay=0.01)
     layer = FusedLinear(256, 512, opt="adamw", hyper=hyper, seed=7)
-    W0 = layer.weight.clone()
+    W0 = P.host_weight(layer.weight, "bf16")
     x = torch.randn(200, 256, device="cuda").to(torch.bfloat16).requires_grad_(True)
     dy = (torch.randn(200, 512, device="cuda") * 1e-2).to(torch.bfloat16)
     y = layer(x)
-    torch.testing.assert_close(y, x.detach() @ W0.t(), rtol=0, atol=0)
     y.backward(dy)
     torch.cuda.synchronize()
-    dX = torch.empty(200, 256, dtype=torch.bfloat16, device="cuda")
-    lib.dgrad(dy, W0, dX)
-    W = W0.clone()
-    m = torch.zeros(512, 256, device="cuda")
-    v = torch.zeros(512, 256, device="cuda")
-    lib.wgrad_step(x.detach(), dy, W, m, v, opt="adamw", hyper=hyper, step=1, seed=7)
-    torch.cuda.synchronize()
-    assert torch.equal(x.grad, dX)
-    assert torch.equal(layer.weight, W) and torch.equal(layer.m, m) and torch.equal(layer.v, v)
-    assert layer.step_count == 1 and not torch.equal(layer.weight, W0)
+    X = synth.Operand("bf16", P.host_weight(x.detach(), "bf16"))
+    dY = synth.Operand("bf16", P.host_weight(dy, "bf16"))
+    # dX from the weight before the step
+    P.dx_close(P.host_weight(x.grad, "bf16"), wgrad.decode_operand(dY), numerics.bf16_to_f64(W0), "dX")
+    # the fused step, oracle at step 1 with the layer's seed
+    m0, v0 = wgrad.init_states("adamw", 512, 256, "f32")
+    ref = wgrad.step(X, dY, W0, m0, v0, "adamw", hyper, 1, 7, "bf16", "f32")
+    env = P.envelope("adamw", hyper, 1, ref["g"], P.grad_bound(X, dY), W0, m0, v0, "bf16", "f32")
+    P.compare(ref, P.host_weight(layer.weight, "bf16"), layer.m.cpu().numpy(), layer.v.cpu().numpy(), None,
+              "bf16", "f32", W0, env, tag="autograd step 1")
+    assert layer.step_count == 1 and not np.array_equal(P.host_weight(layer.weight, "bf16"), W0)
 
 
 def test_weight_updates_without_input_grad(lib):

@@ -39,37 +39,10 @@ def _say(*a):
 
 
 def _init_states(opt, state_fmt, rng, N=N, K=K):
-    """Non-trivial previous moments in the rule's domain (v >= 0)."""
-    m, v = wgrad.init_states(opt, N, K, state_fmt)
-    mm = rng.standard_normal((N, K)) * 2e-3
-    vv = np.abs(rng.standard_normal((N, K))) * 1e-5
-    if opt == "adagrad":
-        vv = vv * 10
-    if state_fmt == "f32":
-        m = None if m is None else mm.astype(np.float32)
-        v = None if v is None else vv.astype(np.float32)
-    else:
-        m = None if m is None else numerics.quantize_block64(mm, True)
-        v = None if v is None else numerics.quantize_block64(vv, False)
-    return m, v
+    return P.init_states(opt, state_fmt, rng, N, K)
 
 
-def _compare(ref, got_W, got_m, got_v, pre, w_fmt, state_fmt, W_old, env=None, tag="", lion=None):
-    """env = (lo, hi, moment ranges) from parity.envelope for inputs whose sums are not exact.
-
-    lion = (hyper, step, m_old, v_old) for Lion with exact sums: sign(c) of c = b1 m + (1 - b1) g
-    is still ambiguous where c is within fp32 rounding of 0, so the range with tau = 0 is used.
-    """
-    if env is None and lion is not None:
-        h, t, m_old, v_old = lion
-        env = P.envelope("lion", h, t, ref["g"], np.zeros_like(ref["g"]), W_old, m_old, v_old, w_fmt, state_fmt)
-    lo, hi, mom = env if env is not None else (None, None, {})
-    slack = P.arith_slack(W_old, w_fmt, ref["W64"])
-    P.weight_close(got_W, ref, w_fmt, lo, hi, what=f"{tag} W", slack=slack)
-    if pre is not None:
-        P.preround_close(pre, ref["W64"] if lo is None else lo, ref["W64"] if hi is None else hi, what=f"{tag} W32")
-    P.state_close(got_m, ref["m"], ref["m64"], state_fmt, f"{tag} m", *mom.get("m", (None, None)))
-    P.state_close(got_v, ref["v"], ref["v64"], state_fmt, f"{tag} v", *mom.get("v", (None, None)))
+_compare = P.compare
 
 
 EXACT = [(opt, i, w, s) for opt in synth.OPTIMIZERS
@@ -453,6 +426,30 @@ def test_v2_token_counts(lib, Tn):
 # 512 full tiles and turns the last k-block column into 32 half tiles of 128 x 128 (the 2048 x
 # 4096 shapes above run as half tiles only).
 N3, K3 = 4096, 4224
+
+
+FULL_RULES = [(opt, s) for opt in synth.OPTIMIZERS for s in ("f32", "int8")]
+
+
+@pytest.mark.parametrize("opt,state_fmt", FULL_RULES, ids=["-".join(c) for c in FULL_RULES])
+def test_v2_full_tiles_every_rule_exact_oracle_fed(lib, opt, state_fmt):
+    """Every rule and moment format on the benchmark's 256 x 128 tiles (with their two-half
+    epilogue) and half tiles in one launch, exact-sum inputs, steps 1 and 6 from the oracle's
+    stored state."""
+    rng = np.random.default_rng(43)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(44, N3, K3, "bf16")
+    m, v = _init_states(opt, state_fmt, rng, N3, K3)
+    for i, t in enumerate((1, 6)):
+        _say("v2 full tiles exact oracle-fed", opt, state_fmt, "step", t)
+        X, dY = synth.integer_case(345 + i, T, N3, K3, "bf16")
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 13, "bf16", state_fmt)
+        d = P.DeviceStep(W, m, v, "bf16", state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, 13, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", state_fmt, W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
+        W, m, v = ref["W"], ref["m"], ref["v"]
 
 
 @pytest.mark.parametrize("opt,state_fmt", [("adamw", "f32"), ("lion", "int8")])
