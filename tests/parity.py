@@ -205,13 +205,20 @@ def preround_close(gpu_pre: np.ndarray, lo, hi, what="W before rounding"):
     x = gpu_pre.astype(np.float64)
     tol = 1e-6 + 1e-4 * np.maximum(np.abs(lo), np.abs(hi))
     bad = (x < lo - tol) | (x > hi + tol)
-    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside tolerance"
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance; first: got {x.flat[i]:.9e}, "
+                             f"want [{np.asarray(lo).flat[i]:.9e}, {np.asarray(hi).flat[i]:.9e}]")
 
 
-def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt):
+def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt, dense=False):
     """Range of the oracle's new fp64 weight (and moments) over gradients g' in [g - tau, g + tau].
 
-    Returns (lo, hi, {"m": (lo, hi), "v": (lo, hi)}) for the moments the rule keeps.
+    Returns (lo, hi, {"m": (lo, hi), "v": (lo, hi)}) for the moments the rule keeps.  The
+    range is sampled at 5 points (the rules are monotonic in g' when the moments start from
+    zero); dense=True samples 129 points and, for the Adam family, the neighbourhood of the
+    interior extremum of (b1 m + (1 - b1) g') / sqrt(b2 v + (1 - b2) g'^2), which lies at
+    g* = (1 - b1) b2 v / ((1 - b2) b1 m) once m and v are non-zero.
     """
     W64 = numerics.bf16_to_f64(W_old) if w_fmt == "bf16" else np.asarray(W_old, np.float32).astype(np.float64)
     m64 = None if m_old is None else (m_old.astype(np.float64) if state_fmt == "f32"
@@ -219,6 +226,16 @@ def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt):
     v64 = None if v_old is None else (v_old.astype(np.float64) if state_fmt == "f32"
                                       else numerics.dequantize_block64(*v_old, False))
     pts = [g - tau, g - 0.5 * tau, g, g + 0.5 * tau, g + tau]
+    if dense:
+        pts += [g + tau * f for f in np.linspace(-1.0, 1.0, 129)]
+        if opt in ("adamw", "nadam", "radam") and m64 is not None and v64 is not None:
+            p = optimizers.hyper64(hyper)
+            b1, b2 = p["beta1"], p["beta2"]
+            with np.errstate(divide="ignore", invalid="ignore"):
+                gs = (1 - b1) * b2 * v64 / ((1 - b2) * b1 * m64)
+            gs = np.where(np.isfinite(gs), gs, g)
+            for f in (0.9, 0.95, 0.98, 0.99, 0.995, 1.0, 1.005, 1.01, 1.02, 1.05, 1.1):
+                pts.append(np.clip(gs * f, g - tau, g + tau))
     res = [optimizers.update(opt, hyper, t, gp, W64, m64, v64) for gp in pts]
     zero_in = (g - tau <= 0) & (g + tau >= 0)
     if zero_in.any():
