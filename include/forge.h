@@ -68,8 +68,21 @@ typedef enum forge_dtype {
   FORGE_BF16 = 1,
   FORGE_FP8_E4M3 = 2, /* OCP e4m3 bytes; `scale` -> one fp32 per-tensor scale (value = decode(code) * scale) */
   FORGE_I8_B64 = 3,   /* signed int8 moment, codes -127..127; `scale` -> rows*cols/64 fp32 block absmax */
-  FORGE_U8_B64 = 4    /* non-negative uint8 moment, codes 0..255; `scale` -> rows*cols/64 fp32 block absmax */
+  FORGE_U8_B64 = 4,   /* non-negative uint8 moment, codes 0..255; `scale` -> rows*cols/64 fp32 block absmax */
+  FORGE_I8DYN_B64 = 5, /* signed moment in the dynamic 8-bit map (see below); `scale` as FORGE_I8_B64 */
+  FORGE_U8DYN_B64 = 6  /* non-negative moment in the dynamic 8-bit map; `scale` as FORGE_U8_B64 */
 } forge_dtype;
+
+/* 8-bit moments (Technical Summary section 2 "Precision and Fidelity": int8 optimizer states in
+ * blocks of 64).  A block is 64 consecutive elements of a row; its fp32 scale is the absmax of
+ * the new values.  The linear map stores code = nearest-even of x * levels / scale (levels 127
+ * signed, 255 unsigned).  The dynamic map (the dynamic tree code of common 8-bit optimizers,
+ * offered for comparison) stores a sign bit (signed only), then in the 7 (signed) or 8
+ * (unsigned) magnitude bits p a run of E zero bits, an indicator bit and F = bits - 1 - E
+ * fraction bits f, for the magnitude scale * 10^-E * (0.1 + 0.9 (f + 1) / 2^F) (p = 0: zero),
+ * nearest magnitude on encoding.  Both maps: a non-zero second moment never stores zero; a
+ * block holding NaN or an infinity stores zero codes and a NaN scale.  m and v of one call
+ * must use the same map. */
 
 typedef enum forge_opt {
   FORGE_ADAMW = 0,        /* states m, v */

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libforge.so")
 
 OPT = {"adamw": 0, "nadam": 1, "radam": 2, "lion": 3, "rmsprop": 4, "adagrad": 5, "sgd": 6, "sgd_momentum": 7}
-F32, BF16, FP8_E4M3, I8_B64, U8_B64 = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3, I8_B64, U8_B64, I8DYN_B64, U8DYN_B64 = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "FORGE_OK", 1: "FORGE_ERR_ARG", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_DTYPE", 4: "FORGE_ERR_LAYOUT",
           5: "FORGE_ERR_ALIAS", 6: "FORGE_ERR_DEVICE", 7: "FORGE_ERR_LAUNCH"}
 SCALARS = ("decay", "l2", "c1", "c2", "c3", "b1", "omb1", "b2", "omb2", "eps", "lr", "rectified")
@@ -94,7 +94,7 @@ def _check(status: int):
         raise ForgeError(status, _lib().forge_last_error().decode())
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, dyn: bool = False) -> int:
     import torch
     if t.dtype == torch.float32:
         return F32
@@ -103,9 +103,9 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float8_e4m3fn:
         return FP8_E4M3
     if t.dtype == torch.int8:
-        return I8_B64
+        return I8DYN_B64 if dyn else I8_B64
     if t.dtype == torch.uint8:
-        return U8_B64
+        return U8DYN_B64 if dyn else U8_B64
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -121,18 +121,18 @@ def _scale_count(code: int, rows: int, cols: int) -> Optional[int]:
     """Element count of the scale buffer a format needs (None: the format has no scale)."""
     if code == FP8_E4M3:
         return 1
-    if code in (I8_B64, U8_B64):
+    if code in (I8_B64, U8_B64, I8DYN_B64, U8DYN_B64):
         return rows * cols // 64
     return None
 
 
-def _tensor(t, scale=None) -> Optional[Tensor]:
+def _tensor(t, scale=None, dyn: bool = False) -> Optional[Tensor]:
     import torch
     if t is None:
         return None
     if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
         raise ValueError("tensors must be 2-D with unit column stride")
-    code = _dtype_code(t)
+    code = _dtype_code(t, dyn)
     want = _scale_count(code, t.shape[0], t.shape[1])
     if scale is not None:
         if want is None:
@@ -180,13 +180,21 @@ def _opts(w_preround_out, sr, W):
     return StepOpts(None if w_preround_out is None else w_preround_out.data_ptr(), 1 if sr else 0)
 
 
+def _dyn(state_map: str) -> bool:
+    if state_map not in ("linear", "dynamic"):
+        raise ValueError(f"state_map must be 'linear' or 'dynamic' (got {state_map!r})")
+    return state_map == "dynamic"
+
+
 def wgrad_step(X, dY, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
                x_scale=None, dy_scale=None, m_scale=None, v_scale=None, w_preround_out=None, sr=True,
-               stream=None):
-    """Fused step: W, m, v updated in place from g = dY^T X (forge_wgrad_step)."""
+               state_map="linear", stream=None):
+    """Fused step: W, m, v updated in place from g = dY^T X (forge_wgrad_step).  8-bit moments
+    (int8 m, uint8 v with block scales) use the linear absmax map, or the dynamic map with
+    state_map="dynamic"."""
     o = _opts(w_preround_out, sr, W)
     _check(_lib().forge_wgrad_step(_ref(_tensor(X, x_scale)), _ref(_tensor(dY, dy_scale)), _ref(_tensor(W)),
-                                   _ref(_tensor(m, m_scale)), _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)),
+                                   _ref(_tensor(m, m_scale, _dyn(state_map))), _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)),
                                    _opt(opt), int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 
@@ -196,12 +204,12 @@ def dgrad(dY, W, dX, *, stream=None):
 
 
 def linear_backward_step(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
-                         m_scale=None, v_scale=None, w_preround_out=None, sr=True, stream=None):
+                         m_scale=None, v_scale=None, w_preround_out=None, sr=True, state_map="linear", stream=None):
     """dgrad then the fused step, in that order (forge_linear_backward_step)."""
     o = _opts(w_preround_out, sr, W)
     _check(_lib().forge_linear_backward_step(
-        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale)),
-        _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, _dyn(state_map))),
+        _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 
@@ -212,11 +220,11 @@ def wgrad_gemm(X, dY, dW, *, x_scale=None, dy_scale=None, stream=None):
 
 
 def optimizer_step(dW, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int, m_scale=None,
-                   v_scale=None, w_preround_out=None, sr=True, stream=None):
+                   v_scale=None, w_preround_out=None, sr=True, state_map="linear", stream=None):
     """Unfused phase 2: the rule applied to a materialised gradient (forge_optimizer_step)."""
     o = _opts(w_preround_out, sr, W)
-    _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale)),
-                                       _ref(_tensor(v, v_scale)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+    _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale, _dyn(state_map))),
+                                       _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
                                        int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 

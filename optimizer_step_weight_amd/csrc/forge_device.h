@@ -142,17 +142,82 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
 // ------------------------------------------------------------------ int8 block-64 requantisation
+// Two 8-bit maps of a block's values x / s (s = the block absmax), selected per call:
+//  * linear: code = nearest-even of x * levels / s, levels 127 (signed, codes -127..127) or
+//    255 (unsigned, 0..255);
+//  * dynamic (the dynamic tree code of common 8-bit optimizers): a sign bit (signed maps only),
+//    then in the B = 7 (signed) or 8 (unsigned) magnitude bits p a run of E zero bits, an
+//    indicator bit and F = B - 1 - E fraction bits f; magnitude 10^-E (0.1 + 0.9 (f + 1) / 2^F),
+//    i.e. the decade (10^-(E+1), 10^-E] in 2^F equal steps, p = 0 meaning 0.  Encoding takes
+//    the nearest magnitude.
+// Both: an unsigned (second-moment) value above zero never stores code 0 (otherwise the next
+// step's denominator would lose that element's history while its first moment keeps it); a
+// block of zeros stores zero codes with scale 0; a block holding a NaN or an infinity stores
+// zero codes and a NaN scale, so it dequantises to NaN and stays visible.
+
+// 10^-e for e = 0..7 (fp32)
+__device__ __forceinline__ float pow10_neg(int e) {
+  float r = 1.0f;
+  r = e == 1 ? 1e-1f : r;
+  r = e == 2 ? 1e-2f : r;
+  r = e == 3 ? 1e-3f : r;
+  r = e == 4 ? 1e-4f : r;
+  r = e == 5 ? 1e-5f : r;
+  r = e == 6 ? 1e-6f : r;
+  r = e == 7 ? 1e-7f : r;
+  return r;
+}
+__device__ __forceinline__ float pow10_pos(int e) {
+  float r = 1.0f;
+  r = e == 1 ? 1e1f : r;
+  r = e == 2 ? 1e2f : r;
+  r = e == 3 ? 1e3f : r;
+  r = e == 4 ? 1e4f : r;
+  r = e == 5 ? 1e5f : r;
+  r = e == 6 ? 1e6f : r;
+  r = e == 7 ? 1e7f : r;
+  return r;
+}
+
+// Value of dynamic code c relative to the block absmax.
+template <bool SIGNED>
+__device__ __forceinline__ float dyn_decode(uint32_t c) {
+  constexpr int B = SIGNED ? 7 : 8;
+  const uint32_t p = c & (SIGNED ? 0x7Fu : 0xFFu);
+  const int L = 32 - __builtin_clz(p | 1u);        // bit length of p (1 for p = 0, unused then)
+  const int F = L - 1, E = B - L;
+  const uint32_t f = p & ((1u << F) - 1u);
+  const float mag = p ? pow10_neg(E) * __builtin_fmaf(0.9f * (float)(f + 1u), __builtin_ldexpf(1.0f, -F), 0.1f) : 0.0f;
+  return (SIGNED && (c & 0x80u)) ? -mag : mag;
+}
+
+// Dynamic code of x given inv = 1 / s: the magnitude pattern p of the nearest magnitude.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t dyn_encode(float x, float inv) {
+  constexpr int B = SIGNED ? 7 : 8, EMAX = B - 1;
+  const float y = fminf(fabsf(x) * inv, 1.0f);
+  int E = 0;  // the decade (10^-(E+1), 10^-E] holding y; EMAX for y <= 10^-EMAX
+#pragma unroll
+  for (int k = 1; k <= EMAX; ++k) E += y <= pow10_neg(k) ? 1 : 0;
+  uint32_t p;
+  if (E == EMAX) {
+    // the only magnitudes left are 10^-EMAX and 0
+    p = (y >= 0.5f * pow10_neg(EMAX)) ? 1u : 0u;
+    if (!SIGNED && y > 0.0f) p = 1u;
+  } else {
+    // continuous step index in the decade; -1 is the top of the decade below (10^-(E+1))
+    const int F = B - 1 - E;
+    const float u = (__builtin_fmaf(y, pow10_pos(E), -0.1f)) * (__builtin_ldexpf(1.0f, F) / 0.9f) - 1.0f;
+    const float f = fminf(fmaxf(__builtin_rintf(u), -1.0f), (float)((1 << F) - 1));
+    p = (uint32_t)((int)(1 << F) + (int)f);
+  }
+  return (SIGNED && x < 0.0f && p) ? (p | 0x80u) : p;
+}
+
 // The new values x[0..C) of this lane, part of a 64-element block spread over LANES lanes
-// (lane ^ 1, 2, ... < LANES; all of them active).  Returns the block scale and the codes:
-//  * scale = absmax of the block; code = nearest-even of x * levels / scale, levels 127
-//    (signed, codes -127..127) or 255 (unsigned, codes 0..255);
-//  * an unsigned (second-moment) value above zero never stores code 0, its code is at least 1:
-//    otherwise about one value in eleven of a Gaussian block would store 0, and the next step's
-//    denominator would lose that element's history while its first moment keeps it;
-//  * a block of zeros stores zero codes with scale 0; a block holding a NaN or an infinity
-//    stores zero codes and a NaN scale, so it dequantises to NaN and stays visible.
+// (lane ^ 1, 2, ... < LANES; all of them active).  Returns the block scale and the codes.
 template <bool SIGNED, int C, int LANES>
-__device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&code)[C]) {
+__device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&code)[C], int dyn) {
   float amax = 0.0f;
   int bad = 0;
 #pragma unroll
@@ -166,20 +231,35 @@ __device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&c
     amax = fmaxf(amax, __shfl_xor(amax, o));
     bad |= __shfl_xor(bad, o);
   }
-  const float inv = (!bad && amax > 0.0f) ? (SIGNED ? 127.0f : 255.0f) / amax : 0.0f;
+  const bool use = !bad && amax > 0.0f;
+  if (dyn) {
+    const float inv = use ? 1.0f / amax : 0.0f;
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const float xj = bad ? 0.0f : x[j];
-    float q = __builtin_rintf(xj * inv);
-    if constexpr (SIGNED) {
-      q = fminf(fmaxf(q, -127.0f), 127.0f);
-      code[j] = (uint32_t)(int32_t)q & 0xFFu;
-    } else {
-      q = fminf(fmaxf(q, (xj > 0.0f && inv > 0.0f) ? 1.0f : 0.0f), 255.0f);
-      code[j] = (uint32_t)q;
+    for (int j = 0; j < C; ++j) code[j] = use ? dyn_encode<SIGNED>(x[j], inv) : 0u;
+  } else {
+    const float inv = use ? (SIGNED ? 127.0f : 255.0f) / amax : 0.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const float xj = bad ? 0.0f : x[j];
+      float q = __builtin_rintf(xj * inv);
+      if constexpr (SIGNED) {
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        code[j] = (uint32_t)(int32_t)q & 0xFFu;
+      } else {
+        q = fminf(fmaxf(q, (xj > 0.0f && inv > 0.0f) ? 1.0f : 0.0f), 255.0f);
+        code[j] = (uint32_t)q;
+      }
     }
   }
   return bad ? __builtin_nanf("") : amax;
+}
+
+// Dequantised value of an 8-bit code of either map.
+template <bool SIGNED>
+__device__ __forceinline__ float dequant8(uint32_t c, float scale, int dyn) {
+  if (dyn) return dyn_decode<SIGNED>(c) * scale;
+  const float q = SIGNED ? (float)(int8_t)(c & 0xFFu) : (float)(c & 0xFFu);
+  return q * (scale * (SIGNED ? (1.0f / 127.0f) : (1.0f / 255.0f)));
 }
 
 // ------------------------------------------------------------------ one 16-element segment
@@ -254,11 +334,10 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
 #pragma unroll
         for (int c = 0; c < 4; ++c) m[4 * q + c] = __uint_as_float(x.m[q][c]);
     } else {
-      const float f = x.ms * (1.0f / 127.0f);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) m[4 * q + c] = (float)(int8_t)(x.m[0][q] >> (8 * c)) * f;
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = dequant8<true>(x.m[0][q] >> (8 * c), x.ms, e.qmap);
     }
   }
   if constexpr (HV) {
@@ -268,11 +347,10 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[4 * q + c] = __uint_as_float(x.v[q][c]);
     } else {
-      const float f = x.vs * (1.0f / 255.0f);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[4 * q + c] = (float)((x.v[0][q] >> (8 * c)) & 0xFFu) * f;
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = dequant8<false>(x.v[0][q] >> (8 * c), x.vs, e.qmap);
     }
   }
 
@@ -342,7 +420,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
       }
     } else {
       uint32_t code[16];
-      const float scale = quant_block64<true, 16, 4>(m, code);
+      const float scale = quant_block64<true, 16, 4>(m, code, e.qmap);
       u32x4 a;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -363,7 +441,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
       }
     } else {
       uint32_t code[16];
-      const float scale = quant_block64<false, 16, 4>(v, code);
+      const float scale = quant_block64<false, 16, 4>(v, code, e.qmap);
       u32x4 a;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -476,9 +554,8 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
 #pragma unroll
       for (int c = 0; c < 4; ++c) m[c] = __uint_as_float(x.m[c]);
     } else {
-      const float f = x.ms * (1.0f / 127.0f);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) m[c] = (float)(int8_t)(x.m.x >> (8 * c)) * f;
+      for (int c = 0; c < 4; ++c) m[c] = dequant8<true>(x.m.x >> (8 * c), x.ms, e.qmap);
     }
   }
   if constexpr (HV) {
@@ -486,9 +563,8 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
 #pragma unroll
       for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(x.v[c]);
     } else {
-      const float f = x.vs * (1.0f / 255.0f);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = (float)((x.v.x >> (8 * c)) & 0xFFu) * f;
+      for (int c = 0; c < 4; ++c) v[c] = dequant8<false>(x.v.x >> (8 * c), x.vs, e.qmap);
     }
   }
 
@@ -534,7 +610,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       st16(static_cast<float*>(e.m) + i0, a);
     } else {
       uint32_t code[4];
-      const float scale = quant_block64<true, 4, 16>(m, code);
+      const float scale = quant_block64<true, 4, 16>(m, code, e.qmap);
       st4(static_cast<int8_t*>(e.m) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
       if (leader) e.m_scale[i0 >> 6] = scale;
     }
@@ -547,7 +623,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       st16(static_cast<float*>(e.v) + i0, a);
     } else {
       uint32_t code[4];
-      const float scale = quant_block64<false, 4, 16>(v, code);
+      const float scale = quant_block64<false, 4, 16>(v, code, e.qmap);
       st4(static_cast<uint8_t*>(e.v) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
       if (leader) e.v_scale[i0 >> 6] = scale;
     }

@@ -44,6 +44,7 @@ struct EpiArgs {
   uint64_t seed;
   uint64_t step;
   int32_t sr;      // bf16 weight: stochastic (1) or nearest-even (0) rounding
+  int32_t qmap;    // 8-bit moments: linear absmax map (0) or dynamic map (1)
   OptScalars s;
 };
 

@@ -21,11 +21,12 @@ On-Register Gradient Elimination for Memory-Efficient LLM Training"):
 Modules:
   philox      Philox4x64-10 counter-based generator (Salmon et al., SC'11).
   numerics    bf16 / e4m3 decoding, bf16 stochastic and nearest rounding,
-              block-64 int8 moment codec.
+              block-64 int8 moment codec (linear absmax map).
+  dynmap      the dynamic 8-bit map for block-64 moments (comparison format).
   optimizers  per-step scalars and the eight element-wise update rules.
   wgrad       dW, dX, and the full and tiled step schedules.
 
 Every function is pinned by tests under tests/ (marked "not gpu") against
 library routines, closed forms, brute force and invariants.
 """
-from . import philox, numerics, optimizers, wgrad  # noqa: F401
+from . import philox, numerics, dynmap, optimizers, wgrad  # noqa: F401

@@ -133,12 +133,15 @@ def levels(signed: bool) -> int:
     return 127 if signed else 255
 
 
-def quantize_block64(x64: np.ndarray, signed: bool):
-    """Quantise a [rows, cols] moment (cols % 64 == 0) -> (codes, fp32 scales[rows, cols/64])."""
+def quantize_blocks(x64: np.ndarray, signed: bool, block: int = BLOCK):
+    """Quantise a [rows, cols] moment in blocks of `block` consecutive row elements (the last
+    block of a row may be shorter) -> (codes, fp32 scales [rows, ceil(cols / block)])."""
     x = np.asarray(x64, dtype=np.float64)
     rows, cols = x.shape
-    assert cols % BLOCK == 0
-    xb = x.reshape(rows, cols // BLOCK, BLOCK)
+    nb = -(-cols // block)
+    xp = np.zeros((rows, nb * block))
+    xp[:, :cols] = x
+    xb = xp.reshape(rows, nb, block)
     finite = np.isfinite(xb).all(axis=2)
     with np.errstate(invalid="ignore", over="ignore"):
         s = np.where(finite, np.max(np.abs(np.where(np.isfinite(xb), xb, 0.0)), axis=2), np.nan).astype(np.float32)
@@ -151,10 +154,20 @@ def quantize_block64(x64: np.ndarray, signed: bool):
     else:
         q = np.where(use[..., None] & (xb > 0), np.maximum(q, 1.0), q)
         codes = np.clip(q, 0, 255).astype(np.uint8)
-    return codes.reshape(rows, cols), s
+    return np.ascontiguousarray(codes.reshape(rows, nb * block)[:, :cols]), s
+
+
+def quantize_block64(x64: np.ndarray, signed: bool):
+    """Quantise a [rows, cols] moment (cols % 64 == 0) -> (codes, fp32 scales[rows, cols/64])."""
+    assert np.shape(x64)[1] % BLOCK == 0
+    return quantize_blocks(x64, signed, BLOCK)
+
+
+def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, signed: bool, block: int = BLOCK) -> np.ndarray:
+    rows, cols = codes.shape
+    s = np.repeat(scales.astype(np.float64), block, axis=1)[:, :cols]
+    return codes.astype(np.float64) * s / levels(signed)
 
 
 def dequantize_block64(codes: np.ndarray, scales: np.ndarray, signed: bool) -> np.ndarray:
-    rows, cols = codes.shape
-    c = codes.astype(np.float64).reshape(rows, cols // BLOCK, BLOCK)
-    return (c * scales.astype(np.float64)[..., None] / levels(signed)).reshape(rows, cols)
+    return dequantize_blocks(codes, scales, signed, BLOCK)

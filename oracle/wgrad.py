@@ -24,7 +24,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from . import numerics, optimizers
+from . import dynmap, numerics, optimizers
 
 TILE = 128
 
@@ -68,13 +68,27 @@ def _decode_w(W, w_fmt):
     return numerics.bf16_to_f64(W) if w_fmt == "bf16" else np.asarray(W, np.float32).astype(np.float64)
 
 
+def _codec(state_fmt):
+    """The 8-bit moment map of a state format: "int8" linear absmax, "int8dyn" dynamic."""
+    if state_fmt == "int8":
+        return numerics
+    if state_fmt == "int8dyn":
+        return dynmap
+    raise ValueError(state_fmt)
+
+
 def _decode_state(st, state_fmt, signed):
     if st is None:
         return None
     if state_fmt == "f32":
         return np.asarray(st, np.float32).astype(np.float64)
     codes, scales = st
-    return numerics.dequantize_block64(codes, scales, signed)
+    return _codec(state_fmt).dequantize_block64(codes, scales, signed)
+
+
+def decode_state(st, state_fmt, signed):
+    """float64 values of a stored moment (fp32 array or (codes, scales))."""
+    return _decode_state(st, state_fmt, signed)
 
 
 def _encode_state(x64, state_fmt, signed):
@@ -82,7 +96,7 @@ def _encode_state(x64, state_fmt, signed):
         return None
     if state_fmt == "f32":
         return x64.astype(np.float32)
-    return numerics.quantize_block64(x64, signed)
+    return _codec(state_fmt).quantize_block64(x64, signed)
 
 
 def _zero_state(N, K, state_fmt, signed):

@@ -27,7 +27,7 @@ import numpy as np
 import torch
 
 import synth
-from oracle import numerics, optimizers, wgrad
+from oracle import dynmap, numerics, optimizers, wgrad
 
 U32 = 2.0 ** -24
 
@@ -86,12 +86,17 @@ class DeviceStep:
         self.m, self.ms = dev_state(m, state_fmt, True)
         self.v, self.vs = dev_state(v, state_fmt, False)
 
+    @property
+    def state_map(self):
+        return "dynamic" if self.state_fmt == "int8dyn" else "linear"
+
     def fused(self, lib, X: synth.Operand, dY: synth.Operand, opt, hyper, step, seed, preround=False, sr=True):
         Xd, xs = dev_operand(X)
         Dd, ds = dev_operand(dY)
         pre = torch.empty(self.W.shape, dtype=torch.float32, device="cuda") if preround else None
         lib.wgrad_step(Xd, Dd, self.W, self.m, self.v, opt=opt, hyper=hyper, step=step, seed=seed,
-                       x_scale=xs, dy_scale=ds, m_scale=self.ms, v_scale=self.vs, w_preround_out=pre, sr=sr)
+                       x_scale=xs, dy_scale=ds, m_scale=self.ms, v_scale=self.vs, w_preround_out=pre, sr=sr,
+                       state_map=self.state_map)
         return pre
 
     def unfused(self, lib, X, dY, opt, hyper, step, seed, preround=False, sr=True):
@@ -101,7 +106,7 @@ class DeviceStep:
         lib.wgrad_gemm(Xd, Dd, dW, x_scale=xs, dy_scale=ds)
         pre = torch.empty(self.W.shape, dtype=torch.float32, device="cuda") if preround else None
         lib.optimizer_step(dW, self.W, self.m, self.v, opt=opt, hyper=hyper, step=step, seed=seed,
-                           m_scale=self.ms, v_scale=self.vs, w_preround_out=pre, sr=sr)
+                           m_scale=self.ms, v_scale=self.vs, w_preround_out=pre, sr=sr, state_map=self.state_map)
         return pre, dW
 
     def host(self):
@@ -152,10 +157,21 @@ def moment_close(gpu: np.ndarray, ref64: np.ndarray, what: str, lo=None, hi=None
                              f"want [{lo.flat[i]:.9e}, {hi.flat[i]:.9e}]")
 
 
-def int8_state_close(gpu, ref, what: str):
+def code_rank(codes: np.ndarray, state_fmt: str) -> np.ndarray:
+    """Position of 8-bit codes in value order: the code itself for the linear map (int8 signed,
+    uint8 unsigned); sign and magnitude pattern for the dynamic map, whose magnitudes increase
+    with the 7 (signed) or 8 (unsigned) magnitude bits."""
+    c = np.asarray(codes)
+    if state_fmt == "int8dyn" and c.dtype == np.int8:
+        u = c.view(np.uint8).astype(np.int64)
+        return np.where(u & 0x80, -(u & 0x7F), u & 0x7F)
+    return c.astype(np.int64)
+
+
+def int8_state_close(gpu, ref, what: str, state_fmt: str = "int8"):
     (gc, gs), (rc, rs) = gpu, ref
-    d = np.abs(gc.astype(np.int64) - rc.astype(np.int64))
-    assert d.max(initial=0) <= 1, f"{what}: int8 codes differ by {int(d.max())}"
+    d = np.abs(code_rank(gc, state_fmt) - code_rank(rc, state_fmt))
+    assert d.max(initial=0) <= 1, f"{what}: 8-bit codes differ by {int(d.max())} steps"
     np.testing.assert_allclose(gs, rs, rtol=1e-4, atol=0, err_msg=f"{what} block scales")
 
 
@@ -166,7 +182,7 @@ def state_close(gpu, ref_stored, ref64, state_fmt, what, lo=None, hi=None):
     if state_fmt == "f32":
         moment_close(gpu, ref64, what, lo, hi)
     else:
-        int8_state_close(gpu, ref_stored, what)
+        int8_state_close(gpu, ref_stored, what, state_fmt)
 
 
 def arith_slack(W_old, w_fmt, W_new64) -> np.ndarray:
@@ -221,10 +237,8 @@ def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt, dense
     g* = (1 - b1) b2 v / ((1 - b2) b1 m) once m and v are non-zero.
     """
     W64 = numerics.bf16_to_f64(W_old) if w_fmt == "bf16" else np.asarray(W_old, np.float32).astype(np.float64)
-    m64 = None if m_old is None else (m_old.astype(np.float64) if state_fmt == "f32"
-                                      else numerics.dequantize_block64(*m_old, True))
-    v64 = None if v_old is None else (v_old.astype(np.float64) if state_fmt == "f32"
-                                      else numerics.dequantize_block64(*v_old, False))
+    m64 = wgrad.decode_state(m_old, state_fmt, True)
+    v64 = wgrad.decode_state(v_old, state_fmt, False)
     pts = [g - tau, g - 0.5 * tau, g, g + 0.5 * tau, g + tau]
     if dense:
         pts += [g + tau * f for f in np.linspace(-1.0, 1.0, 129)]
@@ -314,8 +328,9 @@ def init_states(opt, state_fmt, rng, N, K):
         m = None if m is None else mm.astype(np.float32)
         v = None if v is None else vv.astype(np.float32)
     else:
-        m = None if m is None else numerics.quantize_block64(mm, True)
-        v = None if v is None else numerics.quantize_block64(vv, False)
+        q = dynmap if state_fmt == "int8dyn" else numerics
+        m = None if m is None else q.quantize_block64(mm, True)
+        v = None if v is None else q.quantize_block64(vv, False)
     return m, v
 
 

@@ -545,3 +545,54 @@ def test_v8_token_counts(lib, Tn):
     pre = d.fused(lib, X, dY, "adamw", h, 1, 8, preround=True)
     gW, gm, gv = d.host()
     _compare(ref, gW, gm, gv, pre.cpu().numpy(), "bf16", "f32", W, tag=f"fp8 T={Tn}")
+
+
+# ----------------------------------------------------------------------------- dynamic 8-bit map
+# Moments in the dynamic 8-bit map (the comparison format of common 8-bit optimizers), every
+# rule, on the register-staged path (256 x 384), the bf16 LDS-DMA full and half tiles
+# (4096 x 4224) and the fp8 path; exact-sum inputs, steps 1 and 6 from the oracle's stored state.
+# Codes are compared in value order (within one step).
+DYN = ([(opt, "bf16", N, K) for opt in synth.OPTIMIZERS] + [(opt, "bf16", N3, K3) for opt in synth.OPTIMIZERS]
+       + [("adamw", "fp8", N3, K3), ("lion", "fp8", N3, K3), ("rmsprop", "f32", N, K)])
+
+
+@pytest.mark.parametrize("opt,in_fmt,Nn,Kn", DYN, ids=[f"{o}-{i}-{n}x{k}" for o, i, n, k in DYN])
+def test_dynamic_map_exact_oracle_fed(lib, opt, in_fmt, Nn, Kn):
+    if "m" not in optimizers.STATES[opt] and "v" not in optimizers.STATES[opt]:
+        pytest.skip("the rule keeps no moment")
+    rng = np.random.default_rng(71)
+    h = synth.default_hyper(opt)
+    w_fmt = "f32" if in_fmt == "f32" else "bf16"
+    W = synth.random_weight(72, Nn, Kn, w_fmt)
+    m, v = _init_states(opt, "int8dyn", rng, Nn, Kn)
+    for i, t in enumerate((1, 6)):
+        _say("dynamic map exact oracle-fed", opt, in_fmt, Nn, Kn, "step", t)
+        X, dY = synth.integer_case(380 + i, T, Nn, Kn, in_fmt)
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 21, w_fmt, "int8dyn")
+        d = P.DeviceStep(W, m, v, w_fmt, "int8dyn")
+        pre = d.fused(lib, X, dY, opt, h, t, 21, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), w_fmt, "int8dyn", W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+@pytest.mark.parametrize("Nn,Kn", [(N, K), (N3, K3)])
+def test_dynamic_map_fused_equals_unfused_bitwise(lib, Nn, Kn):
+    _say("dynamic map fused vs unfused", Nn, Kn)
+    rng = np.random.default_rng(73)
+    h = synth.default_hyper("adamw")
+    W = synth.random_weight(74, Nn, Kn, "bf16")
+    m, v = _init_states("adamw", "int8dyn", rng, Nn, Kn)
+    X, dY = synth.gaussian_case(385, T, Nn, Kn, "bf16")
+    a = P.DeviceStep(W, m, v, "bf16", "int8dyn")
+    b = P.DeviceStep(W, m, v, "bf16", "int8dyn")
+    pa = a.fused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    pb, _ = b.unfused(lib, X, dY, "adamw", h, 2, 9, preround=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
+    for x, y in zip(a.host(), b.host()):
+        if isinstance(x, tuple):
+            assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+        else:
+            assert np.array_equal(x, y)

@@ -228,3 +228,32 @@ def test_block64_quantisation_beats_block2048():
     codes, scales = numerics.quantize_block64(m, True)
     deq = numerics.dequantize_block64(codes, scales, True)
     assert abs(float(np.sqrt(np.mean((deq - m) ** 2))) - err(m, 64, True)) < 1e-3 * err(m, 64, True) + 1e-12
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_blocks_of_any_size_with_a_ragged_last_block(signed):
+    """Blocks of 2048 on rows of 5120 elements (the Qwen3-14B hidden size): two full blocks and
+    one of 1024.  Each block's scale is its own absmax; the error stays within half a step of
+    its block (or one step for the second-moment floor)."""
+    from oracle import dynmap
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((3, 5120)) * 1e-3
+    if not signed:
+        x = np.abs(x)
+    codes, s = numerics.quantize_blocks(x, signed, 2048)
+    assert s.shape == (3, 3)
+    for b, (c0, c1) in enumerate(((0, 2048), (2048, 4096), (4096, 5120))):
+        assert np.array_equal(s[:, b], np.abs(x[:, c0:c1]).max(1).astype(np.float32))
+    back = numerics.dequantize_blocks(codes, s, signed, 2048)
+    step = np.repeat(s.astype(np.float64), 2048, axis=1)[:, :5120] / (127 if signed else 255)
+    assert np.all(np.abs(back - x) <= step * (1 + 1e-9))
+    dc, ds = dynmap.quantize_blocks(x, signed, 2048)
+    assert np.array_equal(ds, s)
+    # dynamic map: within half a step of the value's decade (10^-(E+1), 10^-E] of the block scale
+    sc = np.repeat(ds.astype(np.float64), 2048, axis=1)[:, :5120]
+    B = 7 if signed else 8
+    y = np.abs(x) / sc
+    E = np.clip(np.ceil(-np.log10(np.maximum(y, 1e-30))) - 1, 0, B - 1)
+    half = 0.5 * 0.9 * 10.0 ** (-E) / 2.0 ** (B - 1 - E) * sc
+    err = np.abs(dynmap.dequantize_blocks(dc, ds, signed, 2048) - x)
+    assert np.all(err <= half * (1 + 1e-9) + 10.0 ** (-(B - 1)) * sc)
