@@ -54,8 +54,10 @@ extern "C" {
 
 typedef enum forge_status {
   FORGE_OK = 0,
-  FORGE_ERR_ARG = 1,    /* null pointer, step < 1, unknown enum, state given/missing for the rule */
-  FORGE_ERR_SHAPE = 2,  /* shapes disagree, N or K not a multiple of 128, N*K >= 2^32 */
+  FORGE_ERR_ARG = 1,    /* null pointer, step < 1, unknown enum, state given/missing for the rule,
+                           hyper-parameters giving a non-finite per-step scalar (see forge_hyper) */
+  FORGE_ERR_SHAPE = 2,  /* shapes disagree, N or K not a multiple of 128, N*K >= 2^32, a tensor
+                           of 2^48 bytes or more */
   FORGE_ERR_DTYPE = 3,  /* unsupported dtype or dtype combination */
   FORGE_ERR_LAYOUT = 4, /* pointer not 16-byte aligned, or row stride ld != cols */
   FORGE_ERR_ALIAS = 5,  /* an output buffer overlaps an input or another output */
@@ -113,11 +115,14 @@ typedef struct forge_tensor {
 #define FORGE_WD_DECOUPLED 1
 #define FORGE_WD_L2 2
 
-/* Hyper-parameters.  Fields a rule does not use are ignored.
+/* Hyper-parameters.  Fields a rule does not use are ignored (never read).
  *   AdamW/NAdam/RAdam: lr, beta1, beta2, eps, weight_decay; NAdam also momentum_decay (psi).
  *   Lion: lr, beta1 (interpolation inside sign), beta2 (moment), weight_decay.
  *   RMSprop: lr, alpha, eps, weight_decay.   AdaGrad: lr, eps, weight_decay.
- *   SGD: lr, weight_decay.   SGD-momentum: lr, momentum, weight_decay. */
+ *   SGD: lr, weight_decay.   SGD-momentum: lr, momentum, weight_decay.
+ * AdamW, NAdam and RAdam need 0 <= beta1, beta2 < 1, and NAdam a finite momentum_decay >= 0;
+ * every per-step scalar derived from the fields (forge_step_scalars) must be finite in fp32.
+ * Anything else: FORGE_ERR_ARG. */
 typedef struct forge_hyper {
   float lr, beta1, beta2, eps, weight_decay;
   int32_t wd_mode;
@@ -143,8 +148,9 @@ typedef struct forge_step_opts {
  *           rounding: element i = n*K + k draws 16 bits from Philox4x64-10 with counter
  *           (i >> 4, step, 0, 0) and key (seed, 0), field (i & 3) of word (i & 15) >> 2, and
  *           stores (bits(fp32 value) + r) >> 16 (NaN stays NaN).
- *   m, v    moments of the rule ([N, K], F32, or I8_B64 for m / U8_B64 for v with their block
- *           scales); must be NULL for a moment the rule does not keep.  Zero them before step 1.
+ *   m, v    moments of the rule ([N, K]: both F32, or I8_B64 for m and U8_B64 for v, or
+ *           I8DYN_B64 and U8DYN_B64, with their block scales); must be NULL for a moment the rule
+ *           does not keep.  Zero them (codes and scales) before step 1.
  *   step    1-based step count used by bias corrections and schedules; must be >= 1.
  *   seed    stochastic-rounding key; give each weight its own seed.
  * Errors: see forge_status.  A weight with several gradient consumers in one step (tied

@@ -69,11 +69,19 @@ bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Every tensor stays below 2^48 bytes, so the size products below (and the kernels' own
+// bounds, which are tighter) cannot overflow 64-bit arithmetic.
+constexpr int64_t kMaxBytes = int64_t(1) << 48;
+
 forge_status check_tensor(const forge_tensor* t, const char* name) {
   if (!t) return fail(FORGE_ERR_ARG, "%s is NULL", name);
   if (t->rows < 0 || t->cols < 0) return fail(FORGE_ERR_SHAPE, "%s has a negative dimension", name);
   if (dtype_size(t->dtype) == 0) return fail(FORGE_ERR_DTYPE, "%s has unknown dtype %d", name, (int)t->dtype);
-  if (t->rows * t->cols > 0 && !t->data) return fail(FORGE_ERR_ARG, "%s->data is NULL", name);
+  int64_t elems = 0, bytes = 0;
+  if (__builtin_mul_overflow(t->rows, t->cols, &elems) || __builtin_mul_overflow(elems, dtype_size(t->dtype), &bytes) ||
+      bytes >= kMaxBytes)
+    return fail(FORGE_ERR_SHAPE, "%s [%lld, %lld] is too large", name, (long long)t->rows, (long long)t->cols);
+  if (elems > 0 && !t->data) return fail(FORGE_ERR_ARG, "%s->data is NULL", name);
   if (!aligned16(t->data)) return fail(FORGE_ERR_LAYOUT, "%s->data is not 16-byte aligned", name);
   if (t->rows > 0 && t->ld != t->cols)
     return fail(FORGE_ERR_LAYOUT, "%s has row stride %lld, expected %lld (contiguous rows)", name, (long long)t->ld,
@@ -102,42 +110,54 @@ forge_status to_status(int herr) {
 }  // namespace
 
 // ------------------------------------------------------------------ per-step scalars
+// fp64 -> fp32 for a per-step scalar; false if it is not finite in fp32.
+static bool to_f32(double x, float* out) {
+  if (!(std::fabs(x) <= 3.4028234663852886e38)) return false;
+  *out = (float)x;
+  return std::isfinite(*out);
+}
+
 static forge_status compute_scalars(int32_t opt, const forge_hyper* h, int64_t step, forge::OptScalars* out) {
   if (!h) return fail(FORGE_ERR_ARG, "hyper is NULL");
   if (opt < FORGE_ADAMW || opt > FORGE_SGD_MOMENTUM) return fail(FORGE_ERR_ARG, "unknown optimizer %d", (int)opt);
   if (step < 1) return fail(FORGE_ERR_ARG, "step must be >= 1 (got %lld)", (long long)step);
   if (h->wd_mode < FORGE_WD_DEFAULT || h->wd_mode > FORGE_WD_L2)
     return fail(FORGE_ERR_ARG, "unknown wd_mode %d", (int)h->wd_mode);
-  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, eps = h->eps, wd = h->weight_decay;
+  const bool adam_family = opt == FORGE_ADAMW || opt == FORGE_NADAM || opt == FORGE_RADAM;
+  if (adam_family && !(h->beta1 >= 0.0f && h->beta1 < 1.0f && h->beta2 >= 0.0f && h->beta2 < 1.0f))
+    return fail(FORGE_ERR_ARG, "beta1 and beta2 must lie in [0, 1) (got %g, %g)", (double)h->beta1, (double)h->beta2);
+  if (opt == FORGE_NADAM && !(h->momentum_decay >= 0.0f && std::isfinite(h->momentum_decay)))
+    return fail(FORGE_ERR_ARG, "NAdam needs a finite momentum_decay >= 0");
+  // fields a rule does not use are not read (they may hold anything)
+  const bool uses_betas = opt == FORGE_ADAMW || opt == FORGE_NADAM || opt == FORGE_RADAM || opt == FORGE_LION;
+  const bool uses_eps = uses_betas ? opt != FORGE_LION : (opt == FORGE_RMSPROP || opt == FORGE_ADAGRAD);
+  const double lr = h->lr, wd = h->weight_decay;
+  const double b1 = uses_betas ? h->beta1 : 0.0, b2 = uses_betas ? h->beta2 : 0.0, eps = uses_eps ? h->eps : 0.0;
   const double t = (double)step;
   const bool dec = h->wd_mode == FORGE_WD_DECOUPLED ||
                    (h->wd_mode == FORGE_WD_DEFAULT && (opt == FORGE_ADAMW || opt == FORGE_LION));
-  forge::OptScalars s{};
-  s.decay = (float)(dec ? 1.0 - lr * wd : 1.0);
-  s.l2 = (float)(dec ? 0.0 : wd);
-  s.b1 = (float)b1;
-  s.omb1 = (float)(1.0 - b1);
-  s.b2 = (float)b2;
-  s.omb2 = (float)(1.0 - b2);
-  s.eps = (float)eps;
-  s.lr = (float)lr;
-  s.rect = 0;
+  double d[12] = {dec ? 1.0 - lr * wd : 1.0, dec ? 0.0 : wd, 0.0, 0.0, 0.0, b1, 1.0 - b1, b2, 1.0 - b2, eps, lr, 0.0};
+  double &c1 = d[2], &c2 = d[3], &c3 = d[4];
+  int32_t rect = 0;
   const double bc1 = 1.0 - std::pow(b1, t), bc2 = 1.0 - std::pow(b2, t);
   switch (opt) {
     case FORGE_ADAMW:
-      s.c1 = (float)(lr / bc1);
-      s.c2 = (float)(1.0 / bc2);
+      c1 = lr / bc1;
+      c2 = 1.0 / bc2;
       break;
     case FORGE_NADAM: {
       // momentum schedule mu_i = beta1 (1 - 0.5 * 0.96^(i psi)); prod_t = mu_1 ... mu_t
+      // Every factor lies in [0, 1], so once prod < 2^-60 both 1 - prod and 1 - prod * mu_next
+      // round to exactly 1 for this and any later factor: the loop stops there with the same
+      // scalars (and its length no longer grows with the step count).
       const double psi = h->momentum_decay;
       double prod = 1.0;
-      for (int64_t i = 1; i <= step; ++i) prod *= b1 * (1.0 - 0.5 * std::pow(0.96, (double)i * psi));
+      for (int64_t i = 1; i <= step && prod >= 0x1p-60; ++i) prod *= b1 * (1.0 - 0.5 * std::pow(0.96, (double)i * psi));
       const double mu = b1 * (1.0 - 0.5 * std::pow(0.96, t * psi));
       const double mu_next = b1 * (1.0 - 0.5 * std::pow(0.96, (t + 1.0) * psi));
-      s.c1 = (float)(lr * (1.0 - mu) / (1.0 - prod));
-      s.c2 = (float)(1.0 / bc2);
-      s.c3 = (float)(lr * mu_next / (1.0 - prod * mu_next));
+      c1 = lr * (1.0 - mu) / (1.0 - prod);
+      c2 = 1.0 / bc2;
+      c3 = lr * mu_next / (1.0 - prod * mu_next);
       break;
     }
     case FORGE_RADAM: {
@@ -145,23 +165,42 @@ static forge_status compute_scalars(int32_t opt, const forge_hyper* h, int64_t s
       const double rho_t = rho_inf - 2.0 * t * std::pow(b2, t) / bc2;
       if (rho_t > 5.0) {
         const double r = std::sqrt((rho_t - 4.0) * (rho_t - 2.0) * rho_inf / ((rho_inf - 4.0) * (rho_inf - 2.0) * rho_t));
-        s.rect = 1;
-        s.c1 = (float)(lr * r * std::sqrt(bc2) / bc1);
+        rect = 1;
+        c1 = lr * r * std::sqrt(bc2) / bc1;
       } else {
-        s.c1 = (float)(lr / bc1);
+        c1 = lr / bc1;
       }
       break;
     }
     case FORGE_RMSPROP:
-      s.b2 = (float)(double)h->alpha;
-      s.omb2 = (float)(1.0 - (double)h->alpha);
+      d[7] = h->alpha;
+      d[8] = 1.0 - (double)h->alpha;
       break;
     case FORGE_SGD_MOMENTUM:
-      s.c1 = (float)(double)h->momentum;
+      c1 = h->momentum;
       break;
     default:
       break;
   }
+  static const char* const names[12] = {"decay", "l2", "c1", "c2", "c3", "b1", "1 - b1", "b2", "1 - b2", "eps", "lr", ""};
+  float f[12];
+  for (int i = 0; i < 11; ++i)
+    if (!to_f32(d[i], &f[i]))
+      return fail(FORGE_ERR_ARG, "the hyper-parameters give a non-finite step scalar %s (%g) at step %lld", names[i],
+                  d[i], (long long)step);
+  forge::OptScalars s{};
+  s.decay = f[0];
+  s.l2 = f[1];
+  s.c1 = f[2];
+  s.c2 = f[3];
+  s.c3 = f[4];
+  s.b1 = f[5];
+  s.omb1 = f[6];
+  s.b2 = f[7];
+  s.omb2 = f[8];
+  s.eps = f[9];
+  s.lr = f[10];
+  s.rect = rect;
   *out = s;
   return FORGE_OK;
 }

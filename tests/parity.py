@@ -227,37 +227,119 @@ def preround_close(gpu_pre: np.ndarray, lo, hi, what="W before rounding"):
                              f"want [{np.asarray(lo).flat[i]:.9e}, {np.asarray(hi).flat[i]:.9e}]")
 
 
+def _adam_critical_points(opt, hyper, t, m64, v64):
+    """Interior extrema of the Adam family's step as a function of the effective gradient x.
+
+    Each rule's step has the form (A + B x) / (sqrt(C + D x^2) + E) (times a positive
+    constant): AdamW and NAdam with v divided by its bias correction, RAdam's rectified branch
+    with v as it is (its other branch is linear in x).  Setting the derivative to zero gives
+    B E S = A D x - B C with S = sqrt(C + D x^2); squared, the quadratic
+    (A^2 D^2 - B^2 E^2 D) x^2 - 2 A B C D x + B^2 C (C - E^2) = 0, whose real roots hold every
+    critical point (they are only candidates: the envelope takes the oracle's value there)."""
+    p = optimizers.hyper64(hyper)
+    s = optimizers.step_scalars(opt, hyper, t)
+    b1, b2, eps = p["beta1"], p["beta2"], p["eps"]
+    if opt == "radam" and not s["rectified"]:
+        return []
+    A, B = b1 * m64, np.full_like(m64, 1.0 - b1)
+    if opt == "nadam":
+        c_g = p["lr"] * (1.0 - s["mu"]) / (1.0 - s["prod"])
+        c_m = p["lr"] * s["mu_next"] / (1.0 - s["prod_next"])
+        A, B = c_m * b1 * m64, np.full_like(m64, c_g + c_m * (1.0 - b1))
+    if opt == "radam":
+        C, D = b2 * v64, 1.0 - b2
+    else:
+        C, D = b2 * v64 / s["bc2"], (1.0 - b2) / s["bc2"]
+    E = eps
+    qa = A * A * D * D - B * B * E * E * D
+    qb = -2.0 * A * B * C * D
+    qc = B * B * C * (C - E * E)
+    out = []
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        disc = qb * qb - 4.0 * qa * qc
+        sq = np.sqrt(np.maximum(disc, 0.0))
+        q = -0.5 * (qb + np.where(qb >= 0, sq, -sq))
+        for r in (q / qa, qc / q, -qc / qb):          # the last one: the root when qa == 0
+            out.append(np.where(np.isfinite(r) & (disc >= 0), r, np.nan))
+    return out
+
+
+def _zoom_extremes(fn, g, tau, lo_v, hi_v, n=129, k=17, rounds=10, chunk=1 << 16):
+    """Per element, the minimum and maximum of fn(g', sel) over g' in [g - tau, g + tau], folded
+    into lo_v / hi_v.  fn maps gradients of the elements `sel` (flat indices) to their values.
+
+    A grid of n points, then `rounds` zooms around the best point: each zoom samples k points
+    over one cell either side of it and shrinks the cell by (k - 1) / 2.  Where the function
+    has one extremum near the best grid point, that point is next to it, so the zoom window
+    holds it; the final cell is 2 tau / (n - 1) / 8^rounds wide.  Elements go in chunks.
+    """
+    gf, tf = g.ravel(), tau.ravel()
+    lo_f, hi_f = np.array(lo_v, np.float64).ravel(), np.array(hi_v, np.float64).ravel()
+    F = np.linspace(-1.0, 1.0, n)
+    S = np.linspace(-1.0, 1.0, k)
+    for c0 in range(0, gf.size, chunk):
+        sel = np.arange(c0, min(gf.size, c0 + chunk))
+        gc, tc = gf[sel], tf[sel]
+        idx = np.arange(sel.size)
+        Xg = gc[None, :] + tc[None, :] * F[:, None]
+        Vg = np.stack([fn(x, sel) for x in Xg])
+        for pick, better in ((np.argmin, np.less), (np.argmax, np.greater)):
+            j = pick(Vg, axis=0)
+            bx, bv = Xg[j, idx], Vg[j, idx]
+            half = 2.0 * tc / (n - 1)
+            for _ in range(rounds):
+                Xs = np.clip(bx[None, :] + half[None, :] * S[:, None], gc - tc, gc + tc)
+                Vs = np.stack([fn(x, sel) for x in Xs])
+                jj = pick(Vs, axis=0)
+                cx, cv = Xs[jj, idx], Vs[jj, idx]
+                b = better(cv, bv)
+                bx, bv = np.where(b, cx, bx), np.where(b, cv, bv)
+                half = half * 2.0 / (k - 1)
+            if pick is np.argmin:
+                lo_f[sel] = np.minimum(lo_f[sel], bv)
+            else:
+                hi_f[sel] = np.maximum(hi_f[sel], bv)
+    return lo_f.reshape(g.shape), hi_f.reshape(g.shape)
+
+
 def envelope(opt, hyper, t, g, tau, W_old, m_old, v_old, w_fmt, state_fmt, dense=False):
     """Range of the oracle's new fp64 weight (and moments) over gradients g' in [g - tau, g + tau].
 
     Returns (lo, hi, {"m": (lo, hi), "v": (lo, hi)}) for the moments the rule keeps.  The
-    range is sampled at 5 points (the rules are monotonic in g' when the moments start from
-    zero); dense=True samples 129 points and, for the Adam family, the neighbourhood of the
-    interior extremum of (b1 m + (1 - b1) g') / sqrt(b2 v + (1 - b2) g'^2), which lies at
-    g* = (1 - b1) b2 v / ((1 - b2) b1 m) once m and v are non-zero.
+    range is the oracle's value at the ends, the midpoints and g itself, and where they lie in
+    the interval, at the point where the effective gradient (g' plus any coupled L2 term) is
+    zero (the minimum of v) and, for the Adam family, at the critical points of its step (the
+    interior extrema of the new weight when the moments are non-zero).  The other moments and
+    rules are monotone in the effective gradient.  dense=True also runs a grid-and-zoom search
+    for the weight's extremes (a check on the candidates above, for few elements).
     """
     W64 = numerics.bf16_to_f64(W_old) if w_fmt == "bf16" else np.asarray(W_old, np.float32).astype(np.float64)
     m64 = wgrad.decode_state(m_old, state_fmt, True)
     v64 = wgrad.decode_state(v_old, state_fmt, False)
+    g = np.asarray(g, np.float64)
+    tau = np.broadcast_to(np.asarray(tau, np.float64), g.shape)
+    p = optimizers.hyper64(hyper)
+    l2 = 0.0 if optimizers.decoupled(opt, p["wd_mode"]) else p["wd"]
     pts = [g - tau, g - 0.5 * tau, g, g + 0.5 * tau, g + tau]
-    if dense:
-        pts += [g + tau * f for f in np.linspace(-1.0, 1.0, 129)]
-        if opt in ("adamw", "nadam", "radam") and m64 is not None and v64 is not None:
-            p = optimizers.hyper64(hyper)
-            b1, b2 = p["beta1"], p["beta2"]
-            with np.errstate(divide="ignore", invalid="ignore"):
-                gs = (1 - b1) * b2 * v64 / ((1 - b2) * b1 * m64)
-            gs = np.where(np.isfinite(gs), gs, g)
-            for f in (0.9, 0.95, 0.98, 0.99, 0.995, 1.0, 1.005, 1.01, 1.02, 1.05, 1.1):
-                pts.append(np.clip(gs * f, g - tau, g + tau))
     res = [optimizers.update(opt, hyper, t, gp, W64, m64, v64) for gp in pts]
-    zero_in = (g - tau <= 0) & (g + tau >= 0)
-    if zero_in.any():
-        z = optimizers.update(opt, hyper, t, np.zeros_like(g), W64, m64, v64)
-        res.append(tuple(None if a is None else np.where(zero_in, a, b) for a, b in zip(z, res[2])))
+    # interior candidates, as effective gradients x (g' = x - l2 W); those outside the range
+    # take the value at g instead
+    cands = [np.zeros_like(g)]
+    if opt in ("adamw", "nadam", "radam") and m64 is not None and v64 is not None:
+        cands += _adam_critical_points(opt, hyper, t, np.broadcast_to(m64, g.shape), np.broadcast_to(v64, g.shape))
+    for x in cands:
+        gp = x - l2 * W64
+        inside = np.isfinite(gp) & (g - tau <= gp) & (g + tau >= gp)
+        if inside.any():
+            z = optimizers.update(opt, hyper, t, np.where(inside, gp, g), W64, m64, v64)
+            res.append(tuple(None if a is None else np.where(inside, a, b) for a, b in zip(z, res[2])))
     outs = [r[0] for r in res]
     lo = np.minimum.reduce(outs)
     hi = np.maximum.reduce(outs)
+    if dense and g.size:
+        flat = lambda a, sel: None if a is None else np.broadcast_to(a, g.shape).ravel()[sel]
+        lo, hi = _zoom_extremes(lambda x, sel: optimizers.update(opt, hyper, t, x, flat(W64, sel), flat(m64, sel),
+                                                                 flat(v64, sel))[0], g, tau, lo, hi)
     mom = {}
     for j, name in ((1, "m"), (2, "v")):
         if res[0][j] is not None:

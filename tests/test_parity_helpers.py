@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import numerics, wgrad
+from oracle import numerics, optimizers, wgrad
 from tests import parity as P
 
 
@@ -90,3 +90,35 @@ def test_dx_check():
     bad.flat[i] = bad.flat[i] + 4
     with pytest.raises(AssertionError):
         P.dx_close(bad, dY64, W64)
+
+
+@pytest.mark.parametrize("opt", ["adamw", "nadam", "radam", "rmsprop"])
+@pytest.mark.parametrize("t", [2, 7])
+def test_envelope_holds_every_gradient_in_the_range(opt, t):
+    """From non-zero moments the Adam family's new weight has interior extrema in g'; the
+    envelope's candidates must bound the oracle's value at every g' of the range.  Checked by
+    brute force on a 4001-point grid per element, over moments that put the extremum inside
+    the range, including tiny v, where eps shapes a narrow peak near zero."""
+    rng = np.random.default_rng(5 + t)
+    n = 3000
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(6, 1, n, "bf16")[0]
+    g = rng.standard_normal(n) * 10.0 ** rng.uniform(-9, -3, n)
+    tau = np.abs(rng.standard_normal(n)) * 10.0 ** rng.uniform(-9, -3, n)
+    m = (rng.standard_normal(n) * 10.0 ** rng.uniform(-9, -3, n)).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 10.0 ** rng.uniform(-20, -6, n)).astype(np.float32)
+    v[::7] = 0.0
+    mm = None if opt == "rmsprop" else m
+    lo, hi, _ = P.envelope(opt, h, t, g, tau, W, mm, v, "bf16", "f32")
+    W64 = numerics.bf16_to_f64(W)
+    # slack: 1e-9 of the width, and a few fp64 rounding steps of the values themselves
+    slack = 1e-9 * (hi - lo) + 32 * 2.0 ** -52 * np.maximum(np.abs(lo), np.abs(hi))
+    worst = 0.0
+    for f in np.linspace(-1.0, 1.0, 4001):
+        w = optimizers.update(opt, h, t, g + f * tau, W64, None if mm is None else mm.astype(np.float64),
+                              v.astype(np.float64))[0]
+        worst = max(worst, float(np.max(np.maximum(w - hi, lo - w) / slack)))
+    assert worst <= 1.0, f"a grid value lies outside the envelope by {worst:.3e} slacks"
+    # the grid-and-zoom search agrees with the candidates
+    lo2, hi2, _ = P.envelope(opt, h, t, g, tau, W, mm, v, "bf16", "f32", dense=True)
+    assert np.max((hi2 - hi) / slack) <= 1.0 and np.max((lo - lo2) / slack) <= 1.0
