@@ -90,6 +90,46 @@ def cpu_baseline(rows: int, steps: int):
                       f"fp64 dW by BLAS ({blas}), fp64 AdamW, Philox stochastic rounding; {dt:.1f} s"}
 
 
+def cpu_oracle_other_workloads(rows: int = 128):
+    """The oracle's throughput on bounded samples of the other workloads (host cores): every
+    layer or case with its full T and K and the first `rows` rows of W (their dY columns), one
+    step; for the Llama block also dgrad on the first `rows` tokens with the whole W.  Input
+    generation is outside the timed regions."""
+    import numpy as np
+
+    import synth
+    from oracle import wgrad
+    res = {}
+    for cfg in (3, 4, 5):
+        w = synth.WORKLOADS[cfg]
+        flop = secs = 0.0
+        cases = [(li, opt, fmt) for li in range(len(w.layers)) for fmt in ((w.in_fmt,) if cfg != 5 else ("bf16", "fp8"))
+                 for opt in w.optimizers]
+        inputs = {}
+        for li, opt, fmt in cases:
+            L = w.layers[li]
+            if (li, fmt) not in inputs:
+                inputs.clear()
+                inputs[(li, fmt)] = synth.layer_inputs(w, 1, li, in_fmt=fmt), synth.layer_weight(w, li)
+            (X, dY), W = inputs[(li, fmt)]
+            dYs = synth.Operand(dY.fmt, np.ascontiguousarray(dY.data[:, :rows]), dY.scale)
+            m, v = wgrad.init_states(opt, rows, L.K, w.state_fmt)
+            t0 = time.perf_counter()
+            wgrad.step(X, dYs, W[:rows], m, v, opt, w.hyper_for(opt), 1, synth.sr_seed(cfg, li), w.w_fmt, w.state_fmt)
+            secs += time.perf_counter() - t0
+            flop += 2.0 * w.T * rows * L.K
+            if w.dgrad:
+                dYt = wgrad.decode_operand(dY)[:rows]
+                t0 = time.perf_counter()
+                wgrad.dgrad_bf16(dYt, wgrad.decode("bf16", W))
+                secs += time.perf_counter() - t0
+                flop += 2.0 * rows * L.N * L.K
+        res[w.name] = {"value": round(flop / secs / 1e12, 6), "unit": "TFLOP/s", "seconds": round(secs, 2),
+                       "sample": f"{len(cases)} layer/rule cases, {rows} rows of W each (full T={w.T} and K), one step"
+                                 + (f"; dgrad on {rows} tokens with the whole W" if w.dgrad else "")}
+    return {"cores": len(os.sched_getaffinity(0)), "kind": "oracle", "workloads": res}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -198,11 +238,15 @@ def clock_during(forge, fn, reps, seconds):
     return round(cycles / (ticks / hz) / 1e6, 1) if ticks > 0 and hz > 0 else None
 
 
-def workload_timings(forge, timer, reps):
+WORKLOAD_PARTS = ("llama", "qwen", "sweep")
+
+
+def workload_timings(forge, timer, reps, parts=WORKLOAD_PARTS):
     """The other workloads' steps on device-generated Gaussian inputs of the same shapes and scales:
     the 7-linear Llama-3.1-8B block (dgrad then the fused step per layer, T = 8192), the Qwen3-14B
-    block with int8 moments (T = 4096), and the 8-rule sweep on W[4096, 4096] (T = 16384) with bf16
-    and fp8 e4m3 inputs."""
+    block with int8 moments (T = 4096; per layer also with fp32 moments and the contraction
+    alone), and the 8-rule sweep on W[4096, 4096] (T = 16384) with bf16 and fp8 e4m3 inputs (and
+    the contraction alone in each)."""
     import torch
 
     import synth
@@ -216,6 +260,33 @@ def workload_timings(forge, timer, reps):
         s = (x.float().abs().max() / 448.0).reshape(1)
         return (x.float() / s).clamp(-448, 448).to(torch.float8_e4m3fn), s
 
+    def p50_of(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        for r in range(n + 2):
+            torch.cuda.synchronize()
+            ev[0].record()
+            fn(r)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return round(float(sorted(times)[len(times) // 2]), 1)
+
+    out = {}
+    if "llama" in parts:
+        out.update(_llama_block(forge, reps, randn))
+    if "qwen" in parts:
+        out.update(_qwen_block(forge, reps, randn, p50_of))
+    if "sweep" in parts:
+        out.update(_sweep(forge, reps, randn, fp8, p50_of))
+    return out
+
+
+def _llama_block(forge, reps, randn):
+    import torch
+
+    import synth
     out = {}
     # Llama-3.1-8B block: dgrad + fused AdamW step per linear
     w = synth.WORKLOADS[3]
@@ -247,7 +318,14 @@ def workload_timings(forge, timer, reps):
         "block_us": pctl(block), "tflops_wgrad_plus_dgrad": round(flop / (b50 * 1e-6) / 1e12, 1),
         "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)}}
     del layers
+    return out
 
+
+def _qwen_block(forge, reps, randn, p50_of):
+    import torch
+
+    import synth
+    out = {}
     # Qwen3-14B block, int8 block-64 moments
     w = synth.WORKLOADS[4]
     T = w.T
@@ -276,11 +354,32 @@ def workload_timings(forge, timer, reps):
                 per_layer[i].append(ev[i].elapsed_time(ev[i + 1]))
     flop = sum(2.0 * T * d["N"] * d["K"] for d in layers)
     b50 = pctl(block)["p50"]
+    # per layer, the same step with fp32 moments and the contraction alone (fp32 dW), to split
+    # the int8 step's time into contraction and epilogue
+    dW = torch.empty(max(d["N"] * d["K"] for d in layers), dtype=torch.float32, device="cuda")
+    f32_us, gemm_us = {}, {}
+    for i, d in enumerate(layers):
+        m32 = torch.zeros((d["N"], d["K"]), device="cuda")
+        v32 = torch.zeros((d["N"], d["K"]), device="cuda")
+        f32_us[d["name"]] = p50_of(lambda r: forge.wgrad_step(d["X"], d["dY"], d["W"], m32, v32, opt="adamw",
+                                                              hyper=w.hyper, step=r + 1, seed=synth.sr_seed(4, i)), reps)
+        del m32, v32
+        gemm_us[d["name"]] = p50_of(lambda r: forge.wgrad_gemm(d["X"], d["dY"], dW[:d["N"] * d["K"]].view(d["N"], d["K"])),
+                                    reps)
+    del dW
     out["qwen3_14b_block_T4096_int8_states"] = {
         "block_us": pctl(block), "tflops": round(flop / (b50 * 1e-6) / 1e12, 1),
-        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)}}
+        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)},
+        "per_layer_fp32_states_us_p50": f32_us, "per_layer_contraction_only_us_p50": gemm_us}
     del layers
+    return out
 
+
+def _sweep(forge, reps, randn, fp8, p50_of):
+    import torch
+
+    import synth
+    out = {}
     # optimizer sweep, W[4096, 4096], T = 16384, bf16 and fp8 inputs
     w = synth.WORKLOADS[5]
     L = w.layers[0]
@@ -314,6 +413,10 @@ def workload_timings(forge, timer, reps):
     for fmt, opt in cases:
         p50 = sweep_case(fmt, opt)
         sweep[f"{opt}-{fmt}"] = {"us_p50": p50, "tflops": round(2.0 * T * L.N * L.K / (p50 * 1e-6) / 1e12, 1)}
+    dW = torch.empty((L.N, L.K), dtype=torch.float32, device="cuda")
+    sweep["contraction_only_us_p50"] = {
+        "bf16": p50_of(lambda r: forge.wgrad_gemm(X, dY, dW), reps),
+        "fp8": p50_of(lambda r: forge.wgrad_gemm(X8, dY8, dW, x_scale=xs, dy_scale=ds), reps)}
     out["sweep_W4096x4096_T16384"] = sweep
     return out
 
@@ -331,6 +434,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-steps", type=int, default=6)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-others", action="store_true",
+                    help="time the oracle on bounded samples of the other workloads (host only) and print it")
+    ap.add_argument("--only", choices=WORKLOAD_PARTS, default=None,
+                    help="run only this part of the other workloads (for profiler runs) and print its timings")
     ap.add_argument("--kernel", choices=["fused", "gemm", "optimizer", "dgrad"], default=None,
                     help="run only this kernel of the headline shape (for profiler runs); prints its time")
     a = ap.parse_args()
@@ -339,6 +446,10 @@ def main():
               "W by whole 256x128 tiles with the full token count on each GPU (tensor parallelism), which needs "
               "no exchange on this path, so the per-GPU figure is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)
+
+    if a.cpu_others:
+        print(json.dumps(cpu_oracle_other_workloads()), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -354,6 +465,9 @@ def main():
         _build.build(verbose=False)
     torch.cuda.set_device(0)
     forge.device_check(0)
+    if a.only is not None:
+        print(json.dumps(workload_timings(forge, Timer(), 5, parts=(a.only,))), flush=True)
+        return
 
     w = synth.WORKLOADS[2]
     L = w.layers[0]
