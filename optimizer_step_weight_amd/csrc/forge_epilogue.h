@@ -139,11 +139,14 @@ __device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& 
   }
 }
 
-// Segment epilogue: 16 consecutive elements of a row per thread (4 per 128-row half), the
-// stored state of the next two segments in flight while one is updated.  Used for int8
-// moments: with 1-byte codes and per-block scales the 4-element units take about 3x more
-// small memory instructions per element than 16-element segments, and the contiguous-lane
-// layout gains little on such narrow data.
+// Segment epilogue: 16 consecutive elements of a row per thread (4 per 128-row half).  Used
+// for int8 moments: with 1-byte codes and per-block scales the 4-element units take about 3x
+// more small memory instructions per element than 16-element segments, and the
+// contiguous-lane layout gains little on such narrow data.  With bf16 weights the next
+// segment's stored state (18 registers with int8 moments) is loaded before the current one is
+// updated, so its latency hides behind that update.  fp32 weights and Lion keep one segment
+// in flight (loaded after the update), which their registers allow without spilling.  The
+// first segment's loads leave before the staging.
 template <int OPT, int WT, int ST, int HALVES, class Stage>
 __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
                                              int k0, Stage&& stage) {
@@ -153,10 +156,9 @@ __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e
     seg_pos(j & 3, row, kseg);
     return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
   };
-  // one segment in flight: the int8 update needs more registers than the fp32 one, and the
-  // accumulators of the second half are still live during the first
-  SegIn x0;
-  seg_load<OPT, WT, ST>(x0, index_of(0), e);
+  constexpr bool AHEAD = WT == FORGE_W_BF16 && OPT != FORGE_OPT_LION;
+  SegIn xs[AHEAD ? 2 : 1];
+  seg_load<OPT, WT, ST>(xs[0], index_of(0), e);
 #pragma unroll
   for (int h = 0; h < HALVES; ++h) {
     stage(h);
@@ -164,10 +166,17 @@ __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int j = 4 * h + s;
+      const bool more = j + 1 < 4 * HALVES;
       float gr[16];
-      staged_grad(st, s, gr);
-      seg_apply<OPT, WT, ST>(gr, index_of(j), x0, e);
-      if (j + 1 < 4 * HALVES) seg_load<OPT, WT, ST>(x0, index_of(j + 1), e);
+      if constexpr (AHEAD) {
+        if (more) seg_load<OPT, WT, ST>(xs[(j + 1) & 1], index_of(j + 1), e);
+        staged_grad(st, s, gr);
+        seg_apply<OPT, WT, ST>(gr, index_of(j), xs[j & 1], e);
+      } else {
+        staged_grad(st, s, gr);
+        seg_apply<OPT, WT, ST>(gr, index_of(j), xs[0], e);
+        if (more) seg_load<OPT, WT, ST>(xs[0], index_of(j + 1), e);
+      }
     }
     __syncthreads();
   }
