@@ -21,9 +21,9 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-con
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The fused kernels of each path and moment / input format are instantiated in their own
 # translation unit, so the sources compile in parallel.
-SOURCES = ["forge_kernels.hip", "forge_fused2_f32.hip", "forge_fused2_q8.hip", "forge_fused8_f32.hip",
-           "forge_fused8_q8.hip", "forge_fused1_f32.hip", "forge_fused1_bf16.hip", "forge_fused1_fp8.hip",
-           "forge_measure.hip", "forge_host.cpp"]
+SOURCES = ["forge_fused2_q8.hip", "forge_fused2_q8d.hip", "forge_fused1_f32.hip", "forge_fused1_bf16.hip",
+           "forge_fused1_fp8.hip", "forge_fused8_q8.hip", "forge_fused8_q8d.hip", "forge_fused2_f32.hip",
+           "forge_fused8_f32.hip", "forge_kernels.hip", "forge_measure.hip", "forge_host.cpp"]
 
 
 def source_hash(root: str = ROOT) -> str:

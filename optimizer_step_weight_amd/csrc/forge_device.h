@@ -216,8 +216,8 @@ __device__ __forceinline__ uint32_t dyn_encode(float x, float inv) {
 
 // The new values x[0..C) of this lane, part of a 64-element block spread over LANES lanes
 // (lane ^ 1, 2, ... < LANES; all of them active).  Returns the block scale and the codes.
-template <bool SIGNED, int C, int LANES>
-__device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&code)[C], int dyn) {
+template <bool SIGNED, bool DYN, int C, int LANES>
+__device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&code)[C]) {
   float amax = 0.0f;
   int bad = 0;
 #pragma unroll
@@ -232,7 +232,7 @@ __device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&c
     bad |= __shfl_xor(bad, o);
   }
   const bool use = !bad && amax > 0.0f;
-  if (dyn) {
+  if constexpr (DYN) {
     const float inv = use ? 1.0f / amax : 0.0f;
 #pragma unroll
     for (int j = 0; j < C; ++j) code[j] = use ? dyn_encode<SIGNED>(x[j], inv) : 0u;
@@ -255,9 +255,9 @@ __device__ __forceinline__ float quant_block64(const float (&x)[C], uint32_t (&c
 }
 
 // Dequantised value of an 8-bit code of either map.
-template <bool SIGNED>
-__device__ __forceinline__ float dequant8(uint32_t c, float scale, int dyn) {
-  if (dyn) return dyn_decode<SIGNED>(c) * scale;
+template <bool SIGNED, bool DYN>
+__device__ __forceinline__ float dequant8(uint32_t c, float scale) {
+  if constexpr (DYN) return dyn_decode<SIGNED>(c) * scale;
   const float q = SIGNED ? (float)(int8_t)(c & 0xFFu) : (float)(c & 0xFFu);
   return q * (scale * (SIGNED ? (1.0f / 127.0f) : (1.0f / 255.0f)));
 }
@@ -337,7 +337,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) m[4 * q + c] = dequant8<true>(x.m[0][q] >> (8 * c), x.ms, e.qmap);
+        for (int c = 0; c < 4; ++c) m[4 * q + c] = dequant8<true, ST == FORGE_S_Q8D>(x.m[0][q] >> (8 * c), x.ms);
     }
   }
   if constexpr (HV) {
@@ -350,7 +350,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[4 * q + c] = dequant8<false>(x.v[0][q] >> (8 * c), x.vs, e.qmap);
+        for (int c = 0; c < 4; ++c) v[4 * q + c] = dequant8<false, ST == FORGE_S_Q8D>(x.v[0][q] >> (8 * c), x.vs);
     }
   }
 
@@ -420,7 +420,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
       }
     } else {
       uint32_t code[16];
-      const float scale = quant_block64<true, 16, 4>(m, code, e.qmap);
+      const float scale = quant_block64<true, ST == FORGE_S_Q8D, 16, 4>(m, code);
       u32x4 a;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -441,7 +441,7 @@ __device__ __forceinline__ void seg_apply(const float (&g)[16], uint32_t i0, con
       }
     } else {
       uint32_t code[16];
-      const float scale = quant_block64<false, 16, 4>(v, code, e.qmap);
+      const float scale = quant_block64<false, ST == FORGE_S_Q8D, 16, 4>(v, code);
       u32x4 a;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -555,7 +555,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       for (int c = 0; c < 4; ++c) m[c] = __uint_as_float(x.m[c]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) m[c] = dequant8<true>(x.m.x >> (8 * c), x.ms, e.qmap);
+      for (int c = 0; c < 4; ++c) m[c] = dequant8<true, ST == FORGE_S_Q8D>(x.m.x >> (8 * c), x.ms);
     }
   }
   if constexpr (HV) {
@@ -564,7 +564,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(x.v[c]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = dequant8<false>(x.v.x >> (8 * c), x.vs, e.qmap);
+      for (int c = 0; c < 4; ++c) v[c] = dequant8<false, ST == FORGE_S_Q8D>(x.v.x >> (8 * c), x.vs);
     }
   }
 
@@ -610,7 +610,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       st16(static_cast<float*>(e.m) + i0, a);
     } else {
       uint32_t code[4];
-      const float scale = quant_block64<true, 4, 16>(m, code, e.qmap);
+      const float scale = quant_block64<true, ST == FORGE_S_Q8D, 4, 16>(m, code);
       st4(static_cast<int8_t*>(e.m) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
       if (leader) e.m_scale[i0 >> 6] = scale;
     }
@@ -623,7 +623,7 @@ __device__ __forceinline__ void unit_apply(const float (&g)[4], uint32_t i0, con
       st16(static_cast<float*>(e.v) + i0, a);
     } else {
       uint32_t code[4];
-      const float scale = quant_block64<false, 4, 16>(v, code, e.qmap);
+      const float scale = quant_block64<false, ST == FORGE_S_Q8D, 4, 16>(v, code);
       st4(static_cast<uint8_t*>(e.v) + i0, code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24));
       if (leader) e.v_scale[i0 >> 6] = scale;
     }

@@ -188,7 +188,7 @@ __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e
 template <int OPT, int WT, int ST, int HALVES, bool SEG_INT8, class Stage>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
                                               int k0, Stage&& stage) {
-  if constexpr (ST == FORGE_S_Q8 && SEG_INT8) seg_epilogue<OPT, WT, ST, HALVES>(g, e, smem, n0, k0, stage);
+  if constexpr (ST != FORGE_S_F32 && SEG_INT8) seg_epilogue<OPT, WT, ST, HALVES>(g, e, smem, n0, k0, stage);
   else unit_epilogue<OPT, WT, ST, HALVES>(g, e, smem, n0, k0, stage);
 }
 

@@ -41,10 +41,12 @@ FusedFn select_fused1(int w_type, int s_type, int opt) {
 #define FORGE_CASE(O)                                                                                       \
   case O:                                                                                                   \
     if (w_type == FORGE_W_BF16)                                                                             \
-      return s_type == FORGE_S_F32 ? fused_step_kernel<IN, FORGE_W_BF16, FORGE_S_F32, O>                     \
-                                   : fused_step_kernel<IN, FORGE_W_BF16, FORGE_S_Q8, O>;                      \
-    return s_type == FORGE_S_F32 ? fused_step_kernel<IN, FORGE_W_F32, FORGE_S_F32, O>                        \
-                                 : fused_step_kernel<IN, FORGE_W_F32, FORGE_S_Q8, O>;
+      return s_type == FORGE_S_F32  ? fused_step_kernel<IN, FORGE_W_BF16, FORGE_S_F32, O>                    \
+             : s_type == FORGE_S_Q8 ? fused_step_kernel<IN, FORGE_W_BF16, FORGE_S_Q8, O>                     \
+                                    : fused_step_kernel<IN, FORGE_W_BF16, FORGE_S_Q8D, O>;                   \
+    return s_type == FORGE_S_F32  ? fused_step_kernel<IN, FORGE_W_F32, FORGE_S_F32, O>                       \
+           : s_type == FORGE_S_Q8 ? fused_step_kernel<IN, FORGE_W_F32, FORGE_S_Q8, O>                        \
+                                  : fused_step_kernel<IN, FORGE_W_F32, FORGE_S_Q8D, O>;
     FORGE_FOR_EACH_OPT(FORGE_CASE)
 #undef FORGE_CASE
   }

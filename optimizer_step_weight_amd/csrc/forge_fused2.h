@@ -3,7 +3,8 @@
 // a launch, and 256 x 256 tiles in one 8-wave workgroup per CU for long token counts.
 // FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism".
 //
-// Instantiated per moment format in forge_fused2_f32.hip and forge_fused2_q8.hip.
+// Instantiated per moment format in forge_fused2_f32.hip, forge_fused2_q8.hip (linear 8-bit
+// map) and forge_fused2_q8d.hip (dynamic 8-bit map).
 #pragma once
 
 #include "forge_epilogue.h"

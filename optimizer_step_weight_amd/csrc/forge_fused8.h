@@ -3,7 +3,8 @@
 // workgroup per CU for long token counts.  FORGE explainer (gist.science), Technical Summary
 // section 2 "Core Mechanism" and section 4 (fp8 composability).
 //
-// Instantiated per moment format in forge_fused8_f32.hip and forge_fused8_q8.hip.
+// Instantiated per moment format in forge_fused8_f32.hip, forge_fused8_q8.hip (linear 8-bit
+// map) and forge_fused8_q8d.hip (dynamic 8-bit map).
 #pragma once
 
 #include "forge_epilogue.h"

@@ -232,7 +232,7 @@ static forge_status validate_step_outputs(int64_t N, int64_t K, forge_tensor* W,
     return fail(FORGE_ERR_ARG, need_m ? "this rule keeps a first moment m: pass it" : "this rule keeps no m: pass NULL");
   if (need_v != (v != nullptr))
     return fail(FORGE_ERR_ARG, need_v ? "this rule keeps a second moment v: pass it" : "this rule keeps no v: pass NULL");
-  int s_type = -1, qmap = -1;
+  int s_type = -1;
   int n = 0;
   outs[n++] = range_of(W->data, bytes_of(W), "W");
   for (int which = 0; which < 2; ++which) {
@@ -241,19 +241,20 @@ static forge_status validate_step_outputs(int64_t N, int64_t K, forge_tensor* W,
     if (!t) continue;
     if ((st = check_tensor(t, name)) != FORGE_OK) return st;
     if (t->rows != N || t->cols != K) return fail(FORGE_ERR_SHAPE, "%s must have the shape of W", name);
-    int ty, map = 0;
+    int ty;
     if (t->dtype == FORGE_F32) ty = forge::FORGE_S_F32;
     else if (t->dtype == (which ? FORGE_U8_B64 : FORGE_I8_B64)) ty = forge::FORGE_S_Q8;
-    else if (t->dtype == (which ? FORGE_U8DYN_B64 : FORGE_I8DYN_B64)) ty = forge::FORGE_S_Q8, map = 1;
+    else if (t->dtype == (which ? FORGE_U8DYN_B64 : FORGE_I8DYN_B64)) ty = forge::FORGE_S_Q8D;
     else
       return fail(FORGE_ERR_DTYPE, "%s must be F32, %s or %s", name, which ? "U8_B64" : "I8_B64",
                   which ? "U8DYN_B64" : "I8DYN_B64");
-    if (s_type >= 0 && ty != s_type) return fail(FORGE_ERR_DTYPE, "m and v must both be fp32 or both be 8-bit");
-    if (qmap >= 0 && map != qmap) return fail(FORGE_ERR_DTYPE, "m and v must use the same 8-bit map");
+    if (s_type >= 0 && ty != s_type)
+      return fail(FORGE_ERR_DTYPE, (s_type == forge::FORGE_S_F32) != (ty == forge::FORGE_S_F32)
+                                       ? "m and v must both be fp32 or both be 8-bit"
+                                       : "m and v must use the same 8-bit map");
     s_type = ty;
-    qmap = map;
     outs[n++] = range_of(t->data, bytes_of(t), name);
-    if (ty == forge::FORGE_S_Q8) {
+    if (ty != forge::FORGE_S_F32) {
       if (!t->scale) return fail(FORGE_ERR_ARG, "%s->scale (block scales) is NULL", name);
       if (!aligned4(t->scale)) return fail(FORGE_ERR_LAYOUT, "%s->scale is not 4-byte aligned", name);
       outs[n++] = range_of(t->scale, N * K / 64 * 4, which ? "v scales" : "m scales");
@@ -282,7 +283,6 @@ static forge_status validate_step_outputs(int64_t N, int64_t K, forge_tensor* W,
   e.seed = seed;
   e.step = (uint64_t)step;
   e.sr = opts ? (opts->sr_enable != 0) : 1;
-  e.qmap = qmap > 0 ? 1 : 0;
   e.s = s;
   return FORGE_OK;
 }

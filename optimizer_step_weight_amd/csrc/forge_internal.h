@@ -20,8 +20,9 @@ enum : int {
 enum : int { FORGE_IN_F32 = 0, FORGE_IN_BF16 = 1, FORGE_IN_FP8 = 2 };
 // weight storage
 enum : int { FORGE_W_F32 = 0, FORGE_W_BF16 = 1 };
-// moment storage
-enum : int { FORGE_S_F32 = 0, FORGE_S_Q8 = 1 };
+// moment storage: fp32, or 8-bit codes with block-64 fp32 scales in the linear absmax map
+// (Q8) or the dynamic map (Q8D)
+enum : int { FORGE_S_F32 = 0, FORGE_S_Q8 = 1, FORGE_S_Q8D = 2 };
 
 // Per-step scalars of a rule, computed on the host in fp64 and rounded to fp32.
 struct OptScalars {
@@ -44,7 +45,6 @@ struct EpiArgs {
   uint64_t seed;
   uint64_t step;
   int32_t sr;      // bf16 weight: stochastic (1) or nearest-even (0) rounding
-  int32_t qmap;    // 8-bit moments: linear absmax map (0) or dynamic map (1)
   OptScalars s;
 };
 

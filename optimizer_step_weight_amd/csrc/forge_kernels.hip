@@ -160,7 +160,7 @@ static bool use_v8(int in_type, const GemmArgs& g) {
 // quads and 16-lane int8 blocks inside them) are either in range or out of it.
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t n_elem, EpiArgs e) {
-  if constexpr (ST == FORGE_S_Q8) {  // int8 moments: 16 consecutive elements per thread (see seg_epilogue)
+  if constexpr (ST != FORGE_S_F32) {  // int8 moments: 16 consecutive elements per thread (see seg_epilogue)
     const int64_t seg = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (seg * 16 >= n_elem) return;  // n_elem % 64 == 0: the 4 lanes of an int8 block leave together
     float gr[16];
@@ -297,13 +297,23 @@ static OptFn opt_for(int opt) {
   return nullptr;
 }
 
+static FusedFn fused2_for(int s_type, int wide, int w_type, int opt) {
+  return s_type == FORGE_S_F32  ? select_fused2<FORGE_S_F32>(wide, w_type, opt)
+         : s_type == FORGE_S_Q8 ? select_fused2<FORGE_S_Q8>(wide, w_type, opt)
+                                : select_fused2<FORGE_S_Q8D>(wide, w_type, opt);
+}
+static FusedFn fused8_for(int s_type, int wide, int w_type, int opt) {
+  return s_type == FORGE_S_F32  ? select_fused8<FORGE_S_F32>(wide, w_type, opt)
+         : s_type == FORGE_S_Q8 ? select_fused8<FORGE_S_Q8>(wide, w_type, opt)
+                                : select_fused8<FORGE_S_Q8D>(wide, w_type, opt);
+}
+
 int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmArgs& g, const EpiArgs& e,
                       void* stream) {
   FusedFn fn = nullptr;
   if (use_v2(in_type, g)) {
-    fn = s_type == FORGE_S_F32 ? select_fused2<FORGE_S_F32>(0, w_type, opt) : select_fused2<FORGE_S_Q8>(0, w_type, opt);
-    FusedFn fw =
-        s_type == FORGE_S_F32 ? select_fused2<FORGE_S_F32>(1, w_type, opt) : select_fused2<FORGE_S_Q8>(1, w_type, opt);
+    fn = fused2_for(s_type, 0, w_type, opt);
+    FusedFn fw = fused2_for(s_type, 1, w_type, opt);
     if (!fn || !fw) return (int)hipErrorInvalidValue;
     GemmArgs g2 = g;
     g2.kb_base = 0;
@@ -327,9 +337,8 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
     return (int)hipGetLastError();
   }
   if (use_v8(in_type, g)) {
-    fn = s_type == FORGE_S_F32 ? select_fused8<FORGE_S_F32>(0, w_type, opt) : select_fused8<FORGE_S_Q8>(0, w_type, opt);
-    FusedFn fw =
-        s_type == FORGE_S_F32 ? select_fused8<FORGE_S_F32>(1, w_type, opt) : select_fused8<FORGE_S_Q8>(1, w_type, opt);
+    fn = fused8_for(s_type, 0, w_type, opt);
+    FusedFn fw = fused8_for(s_type, 1, w_type, opt);
     if (!fn || !fw) return (int)hipErrorInvalidValue;
     GemmArgs g8 = g;
     g8.kb_base = 0;
@@ -389,11 +398,15 @@ int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
 
 int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n_elem, const EpiArgs& e,
                      void* stream) {
-  OptFn fn;
+  OptFn fn = nullptr;
   if (w_type == FORGE_W_BF16)
-    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_BF16, FORGE_S_F32>(opt) : opt_for<FORGE_W_BF16, FORGE_S_Q8>(opt);
+    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_BF16, FORGE_S_F32>(opt)
+         : s_type == FORGE_S_Q8 ? opt_for<FORGE_W_BF16, FORGE_S_Q8>(opt)
+                                : opt_for<FORGE_W_BF16, FORGE_S_Q8D>(opt);
   else
-    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_F32, FORGE_S_F32>(opt) : opt_for<FORGE_W_F32, FORGE_S_Q8>(opt);
+    fn = s_type == FORGE_S_F32 ? opt_for<FORGE_W_F32, FORGE_S_F32>(opt)
+         : s_type == FORGE_S_Q8 ? opt_for<FORGE_W_F32, FORGE_S_Q8>(opt)
+                                : opt_for<FORGE_W_F32, FORGE_S_Q8D>(opt);
   if (!fn) return (int)hipErrorInvalidValue;
   const unsigned grid = (unsigned)((n_elem + 4095) / 4096);   // 4 waves of 1024 elements a block
   hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, dW, n_elem, e);

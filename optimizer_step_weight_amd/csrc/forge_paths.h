@@ -24,8 +24,10 @@ FusedFn select_fused1(int w_type, int s_type, int opt);
 
 extern template FusedFn select_fused2<FORGE_S_F32>(int, int, int);
 extern template FusedFn select_fused2<FORGE_S_Q8>(int, int, int);
+extern template FusedFn select_fused2<FORGE_S_Q8D>(int, int, int);
 extern template FusedFn select_fused8<FORGE_S_F32>(int, int, int);
 extern template FusedFn select_fused8<FORGE_S_Q8>(int, int, int);
+extern template FusedFn select_fused8<FORGE_S_Q8D>(int, int, int);
 extern template FusedFn select_fused1<FORGE_IN_F32>(int, int, int);
 extern template FusedFn select_fused1<FORGE_IN_BF16>(int, int, int);
 extern template FusedFn select_fused1<FORGE_IN_FP8>(int, int, int);
