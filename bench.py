@@ -238,15 +238,16 @@ def clock_during(forge, fn, reps, seconds):
     return round(cycles / (ticks / hz) / 1e6, 1) if ticks > 0 and hz > 0 else None
 
 
-WORKLOAD_PARTS = ("llama", "qwen", "sweep")
+WORKLOAD_PARTS = ("single", "llama", "qwen", "sweep")
 
 
 def workload_timings(forge, timer, reps, parts=WORKLOAD_PARTS):
     """The other workloads' steps on device-generated Gaussian inputs of the same shapes and scales:
-    the 7-linear Llama-3.1-8B block (dgrad then the fused step per layer, T = 8192), the Qwen3-14B
-    block with int8 moments (T = 4096; per layer also with fp32 moments and the contraction
-    alone), and the 8-rule sweep on W[4096, 4096] (T = 16384) with bf16 and fp8 e4m3 inputs (and
-    the contraction alone in each)."""
+    the single fp32 linear (W[256, 256], T = 512), the 7-linear Llama-3.1-8B block (dgrad then the
+    fused step per layer, T = 8192), the Qwen3-14B block with int8 moments (T = 4096; per layer
+    also with fp32 moments and the contraction alone), and the 8-rule sweep on W[4096, 4096]
+    (T = 16384) with bf16 and fp8 e4m3 inputs (and the contraction alone in each).  Each also
+    times its unfused counterpart (GEMM to an fp32 dW, then the optimizer kernel)."""
     import torch
 
     import synth
@@ -274,6 +275,8 @@ def workload_timings(forge, timer, reps, parts=WORKLOAD_PARTS):
         return round(float(sorted(times)[len(times) // 2]), 1)
 
     out = {}
+    if "single" in parts:
+        out.update(_single_fp32(forge, reps, p50_of))
     if "llama" in parts:
         out.update(_llama_block(forge, reps, randn))
     if "qwen" in parts:
@@ -314,11 +317,59 @@ def _llama_block(forge, reps, randn):
                 per_layer[i].append(ev[i].elapsed_time(ev[i + 1]))
     flop = sum(4.0 * T * d["N"] * d["K"] for d in layers)
     b50 = pctl(block)["p50"]
+    # the unfused block: dgrad, the GEMM into one fp32 dW buffer shared by the layers (the
+    # smallest gradient memory an unfused step can have; all 7 alive together would need
+    # 832 MiB), then the optimizer kernel
+    dW = torch.empty(max(d["N"] * d["K"] for d in layers), dtype=torch.float32, device="cuda")
+    ub = []
+    for r in range(reps + 2):
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i, d in enumerate(layers):
+            g = dW[:d["N"] * d["K"]].view(d["N"], d["K"])
+            forge.dgrad(d["dY"], d["W"], d["dX"])
+            forge.wgrad_gemm(d["X"], d["dY"], g)
+            forge.optimizer_step(g, d["W"], d["m"], d["v"], opt="adamw", hyper=w.hyper, step=reps + 3 + r,
+                                 seed=synth.sr_seed(3, i))
+        ev[-1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ub.append(ev[0].elapsed_time(ev[-1]))
+    del dW
     out["llama8b_block_T8192_dgrad_plus_step"] = {
         "block_us": pctl(block), "tflops_wgrad_plus_dgrad": round(flop / (b50 * 1e-6) / 1e12, 1),
-        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)}}
+        "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)},
+        "unfused_block_us": pctl(ub)}
     del layers
     return out
+
+
+def _single_fp32(forge, reps, p50_of):
+    """The single fp32 linear (W[256, 256], T = 512, fp32 everything, no stochastic rounding):
+    fused and unfused."""
+    import torch
+
+    import synth
+    w = synth.WORKLOADS[1]
+    L = w.layers[0]
+    X = torch.randn((w.T, L.K), device="cuda") * w.x_std
+    dY = torch.randn((w.T, L.N), device="cuda") * w.dy_std
+    W = torch.randn((L.N, L.K), device="cuda") * w.w_std
+    m, v = torch.zeros_like(W), torch.zeros_like(W)
+    dW = torch.empty_like(W)
+    # 20 steps back to back between two events, so that the host's per-call time (tens of us
+    # of Python marshalling) overlaps the device's instead of adding to it
+    fused = p50_of(lambda r: [forge.wgrad_step(X, dY, W, m, v, opt="adamw", hyper=w.hyper, step=20 * r + i + 1, seed=1)
+                              for i in range(20)], 10) / 20
+
+    def unf(r):
+        for i in range(20):
+            forge.wgrad_gemm(X, dY, dW)
+            forge.optimizer_step(dW, W, m, v, opt="adamw", hyper=w.hyper, step=1000 + 20 * r + i, seed=1)
+    unfused = p50_of(unf, 10) / 20
+    flop = 2.0 * w.T * L.N * L.K
+    return {"single_fp32_W256x256_T512": {"fused_us": round(fused, 1), "unfused_us": round(unfused, 1),
+                                          "tflops": round(flop / (fused * 1e-6) / 1e12, 3)}}
 
 
 def _qwen_block(forge, reps, randn, p50_of):
@@ -357,7 +408,7 @@ def _qwen_block(forge, reps, randn, p50_of):
     # per layer, the same step with fp32 moments and the contraction alone (fp32 dW), to split
     # the int8 step's time into contraction and epilogue
     dW = torch.empty(max(d["N"] * d["K"] for d in layers), dtype=torch.float32, device="cuda")
-    f32_us, gemm_us = {}, {}
+    f32_us, gemm_us, unfused_us = {}, {}, {}
     for i, d in enumerate(layers):
         m32 = torch.zeros((d["N"], d["K"]), device="cuda")
         v32 = torch.zeros((d["N"], d["K"]), device="cuda")
@@ -366,11 +417,19 @@ def _qwen_block(forge, reps, randn, p50_of):
         del m32, v32
         gemm_us[d["name"]] = p50_of(lambda r: forge.wgrad_gemm(d["X"], d["dY"], dW[:d["N"] * d["K"]].view(d["N"], d["K"])),
                                     reps)
+
+        def unf(r):
+            g = dW[:d["N"] * d["K"]].view(d["N"], d["K"])
+            forge.wgrad_gemm(d["X"], d["dY"], g)
+            forge.optimizer_step(g, d["W"], d["m"], d["v"], opt="adamw", hyper=w.hyper, step=reps + 3 + r,
+                                 seed=synth.sr_seed(4, i), m_scale=d["ms"], v_scale=d["vs"])
+        unfused_us[d["name"]] = p50_of(unf, reps)
     del dW
     out["qwen3_14b_block_T4096_int8_states"] = {
         "block_us": pctl(block), "tflops": round(flop / (b50 * 1e-6) / 1e12, 1),
         "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)},
-        "per_layer_fp32_states_us_p50": f32_us, "per_layer_contraction_only_us_p50": gemm_us}
+        "per_layer_fp32_states_us_p50": f32_us, "per_layer_contraction_only_us_p50": gemm_us,
+        "per_layer_unfused_us_p50": unfused_us, "unfused_block_us_p50": round(sum(unfused_us.values()), 1)}
     del layers
     return out
 
@@ -417,6 +476,18 @@ def _sweep(forge, reps, randn, fp8, p50_of):
     sweep["contraction_only_us_p50"] = {
         "bf16": p50_of(lambda r: forge.wgrad_gemm(X, dY, dW), reps),
         "fp8": p50_of(lambda r: forge.wgrad_gemm(X8, dY8, dW, x_scale=xs, dy_scale=ds), reps)}
+    Wu = randn((L.N, L.K), w.w_std)
+    mu, vu = torch.zeros((L.N, L.K), device="cuda"), torch.zeros((L.N, L.K), device="cuda")
+
+    def unf(fmt):
+        def run(r):
+            if fmt == "bf16":
+                forge.wgrad_gemm(X, dY, dW)
+            else:
+                forge.wgrad_gemm(X8, dY8, dW, x_scale=xs, dy_scale=ds)
+            forge.optimizer_step(dW, Wu, mu, vu, opt="adamw", hyper=w.hyper_for("adamw"), step=r + 1, seed=3)
+        return run
+    sweep["unfused_adamw_us_p50"] = {"bf16": p50_of(unf("bf16"), reps), "fp8": p50_of(unf("fp8"), reps)}
     out["sweep_W4096x4096_T16384"] = sweep
     return out
 

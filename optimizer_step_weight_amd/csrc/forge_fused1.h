@@ -21,17 +21,25 @@ __global__ __launch_bounds__(kThreads, 2) void fused_step_kernel(GemmArgs g, Epi
   floatx4 acc[4][4];
   contract_tile<IN>(acc, smem, g, n0, k0);
 
+  // the thread's 4 segments of 16 elements; the next segment's stored state is in flight while
+  // one is updated, and the first leaves before the staging
+  const int tid = threadIdx.x;
+  auto index_of = [&](int s) {
+    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
+    return (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
+  };
+  SegIn xs[2];
+  seg_load<OPT, WT, ST>(xs[0], index_of(0), e);
   float* st = reinterpret_cast<float*>(smem);
   stage_acc(st, acc, input_scale<IN>(g));
   __syncthreads();
-  const int tid = threadIdx.x;
-#pragma unroll 1
+#pragma unroll
   for (int s = 0; s < 4; ++s) {
+    if (s + 1 < 4) seg_load<OPT, WT, ST>(xs[(s + 1) & 1], index_of(s + 1), e);
     const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
     float gr[16];
     read_seg16(gr, st, row, kseg);
-    const uint32_t i0 = (uint32_t)(n0 + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
-    step_segment16<OPT, WT, ST>(gr, i0, e);
+    seg_apply<OPT, WT, ST>(gr, index_of(s), xs[s & 1], e);
   }
 }
 
