@@ -15,8 +15,8 @@ namespace forge {
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
   int nb, kb;
-  tile_coords_at(b, (int)(g.N / ml2::BM), g.kb_split, nb, kb);
-  const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  tile_coords_at(b, g.nbn, g.kb_split, nb, kb);
+  const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
@@ -27,8 +27,8 @@ __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
   int nb, kb;
-  tile_coords_at(hb, (int)(g.N / ml2::BM_HALF), g.nbk - g.kb_split, nb, kb);
-  const int n0 = nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
+  tile_coords_at(hb, 2 * g.nbn, g.nbk - g.kb_split, nb, kb);
+  const int n0 = g.nb_base * ml2::BM + nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
   ml2::floatx4 acc[4][4];
   ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
@@ -47,7 +47,8 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
 // tiles): both 128-column halves share the dY panel and 4 slabs fit in LDS.  The epilogue is
 // the 256 x 128 tile's, run by each half: threads 0-255 update columns k0 .. k0 + 127 and
 // threads 256-511 columns k0 + 128 .. k0 + 255, each staging through its own LDS buffer.  The
-// launch covers the nbk / 2 wide column blocks from kb_base / 2 on.
+// launch covers the nbn row blocks from nb_base on and the nbk / 2 wide column blocks from
+// kb_base / 2 on.
 constexpr int kSmemW = ml2::WidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::WidePipe::SMEM : 2 * ml2::EPI_BYTES;
 static_assert(kSmemW <= 160 * 1024, "wide tiles fit the CU's LDS");
 
@@ -55,9 +56,9 @@ template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel2w(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemW];
   int nb, kb;
-  tile_coords_at((int)blockIdx.x, (int)(g.N / ml2::BM), g.nbk / 2, nb, kb);
+  tile_coords_at((int)blockIdx.x, g.nbn, g.nbk / 2, nb, kb);
   const int kh = (int)(threadIdx.x >> 8);
-  const int n0 = nb * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
+  const int n0 = (g.nb_base + nb) * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract_wide(acc, smem, g, n0, kw0);
   unsigned char* mine = smem + kh * ml2::EPI_BYTES;

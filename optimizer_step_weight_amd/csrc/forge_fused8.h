@@ -15,13 +15,14 @@ namespace forge {
 // (forge_mainloop8.h); the tensors' scale product multiplies the finished sums at staging.
 static_assert(ml8::SMEM <= kSmem2, "fp8 stages fit the shared buffer size");
 
-// The launch covers the nbk 128-column blocks from kb_base on.
+// The launch covers the nbn 256-row blocks from nb_base on and the nbk 128-column blocks from
+// kb_base on.
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
   int nb, kb;
-  tile_coords((int)(g.N / ml2::BM), g.nbk, nb, kb);
-  const int n0 = nb * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  tile_coords(g.nbn, g.nbk, nb, kb);
+  const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
   ml8::floatx16 acc[4][2];
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
@@ -38,9 +39,9 @@ template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel8w(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem8W];
   int nb, kb;
-  tile_coords_at((int)blockIdx.x, (int)(g.N / ml2::BM), g.nbk / 2, nb, kb);
+  tile_coords_at((int)blockIdx.x, g.nbn, g.nbk / 2, nb, kb);
   const int kh = (int)(threadIdx.x >> 8);
-  const int n0 = nb * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
+  const int n0 = (g.nb_base + nb) * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
   ml8::floatx16 acc[4][2];
   ml8::contract_wide(acc, smem, g, n0, kw0);
   const float scale = g.dy_scale[0] * g.x_scale[0];

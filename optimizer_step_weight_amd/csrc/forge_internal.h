@@ -55,10 +55,11 @@ struct GemmArgs {
   const float* x_scale;   // fp8 per-tensor scales (device), else null
   const float* dy_scale;
   int64_t T, N, K;
-  // 256 x 128 path only: the launch covers the nbk 128-column blocks from kb_base on;
-  // workgroups [0, nfull) take 256 x 128 tiles of blocks [0, kb_split) of that range and the
-  // rest 128 x 128 tiles of blocks [kb_split, nbk) (set by the launcher).
-  int nfull = 0, kb_split = 0, kb_base = 0, nbk = 0;
+  // LDS-DMA paths (set by the launcher): the launch covers the nbn 256-row blocks from nb_base
+  // on and the nbk 128-column blocks from kb_base on; on the 256 x 128 path workgroups
+  // [0, nfull) take 256 x 128 tiles of column blocks [0, kb_split) of that range and the rest
+  // 128 x 128 tiles of column blocks [kb_split, nbk).
+  int nfull = 0, kb_split = 0, kb_base = 0, nbk = 0, nb_base = 0, nbn = 0;
 };
 
 // Launchers (defined in the .hip translation units).  Return a hipError_t as int.

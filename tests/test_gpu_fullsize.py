@@ -91,10 +91,12 @@ def test_exact_down_proj_headline_launch(lib):
         W, m, v = ref["W"], ref["m"], ref["v"]
 
 
-@pytest.mark.parametrize("li", [0, 6], ids=["q_proj", "down_proj"])
+@pytest.mark.parametrize("li", [0, 4, 6], ids=["q_proj", "gate_proj", "down_proj"])
 def test_exact_wide_tiles_T8192_with_dgrad(lib, li):
-    """T = 8192: q_proj runs on 256 x 256 tiles only; down_proj on 48 wide column blocks plus a
-    256 x 128 launch for the last 16 columns of 128.  dgrad first, on the old weight."""
+    """T = 8192: q_proj runs on 256 x 256 tiles only; gate_proj on 48 wide row blocks plus a
+    256 x 128 launch (as half tiles) for its last 8 row blocks; down_proj on 48 wide column
+    blocks plus a 256 x 128 launch for the last 16 columns of 128.  dgrad first, on the old
+    weight."""
     w = synth.WORKLOADS[3]
     L = w.layers[li]
     X, dY = synth.integer_case(2100 + li, w.T, L.N, L.K, "bf16")

@@ -5,7 +5,9 @@ the remaining columns run on the 256 x 128 path in a second launch.  Every eleme
 runs in the same order on both paths, so the fused step must equal the unfused path (the
 256 x 128 GEMM to HBM, then the optimizer kernel) bitwise, whatever mix of launches covers the
 weight.  Shapes (on 256 CUs): 4096 x 4096 is 256 wide tiles (one launch); 2048 x 8192 is 8 x 32
-wide tiles; 4096 x 4224 adds one 128-column block, run as 32 half tiles in the second launch.
+wide tiles; 4096 x 4224 adds one 128-column block, run as 32 half tiles in the second launch;
+6144 x 4096 has no whole-round column split (24 row blocks), so its first 16 row blocks run as
+256 wide tiles and the last 8 on the 256 x 128 path (as 512 half tiles for bf16 inputs).
 T = 8193 and 8200 leave a ragged last slab of tokens.  fp8 inputs follow the same rule.  The
 full-size workload tests (the Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384 in
 bf16 and fp8) check this path against the fp64 oracle on sampled rows.
@@ -44,7 +46,8 @@ CASES = [((4096, 4096), "adamw", "bf16", "f32", 8192), ((4096, 4224), "adamw", "
          ((2048, 8192), "lion", "bf16", "int8", 8193), ((4096, 4096), "nadam", "f32", "f32", 8192),
          ((4096, 4224), "radam", "bf16", "int8", 8192), ((2048, 8192), "rmsprop", "bf16", "f32", 8192),
          ((4096, 4096), "adagrad", "bf16", "f32", 8193), ((4096, 4224), "sgd", "f32", "f32", 8192),
-         ((2048, 8192), "sgd_momentum", "bf16", "int8", 8192)]
+         ((2048, 8192), "sgd_momentum", "bf16", "int8", 8192), ((6144, 4096), "adamw", "bf16", "f32", 8192),
+         ((6144, 4096), "lion", "bf16", "int8", 8200), ((6144, 4096), "adamw", "bf16", "int8dyn", 8192)]
 
 
 @pytest.mark.parametrize("shape,opt,w_fmt,state_fmt,Tn", CASES,
@@ -70,7 +73,8 @@ def test_wide_fused_equals_unfused_bitwise(lib, shape, opt, w_fmt, state_fmt, Tn
 # fp8 e4m3 inputs (per-tensor scales) take the same wide tiles for T >= 8192; the rest of the
 # columns run on the 256 x 128 fp8 kernel.
 CASES8 = [((4096, 4096), "adamw", "bf16", "f32", 8192), ((4096, 4224), "nadam", "bf16", "int8", 8200),
-          ((4096, 4096), "lion", "f32", "f32", 8193), ((2048, 8192), "sgd", "bf16", "f32", 8192)]
+          ((4096, 4096), "lion", "f32", "f32", 8193), ((2048, 8192), "sgd", "bf16", "f32", 8192),
+          ((6144, 4096), "radam", "bf16", "f32", 8192)]
 
 
 @pytest.mark.parametrize("shape,opt,w_fmt,state_fmt,Tn", CASES8,
