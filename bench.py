@@ -303,7 +303,13 @@ def _llama_block(forge, reps, randn):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
     per_layer = [[] for _ in layers]
     block = []
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
     for r in range(reps + 2):
+        if r == 1:  # the peak memory of one whole fused block step (the first iteration)
+            torch.cuda.synchronize()
+            fused_extra = torch.cuda.max_memory_allocated() - base
         torch.cuda.synchronize()
         ev[0].record()
         for i, d in enumerate(layers):
@@ -336,10 +342,28 @@ def _llama_block(forge, reps, randn):
         if r >= 2:
             ub.append(ev[0].elapsed_time(ev[-1]))
     del dW
+    # the gradient floor of a framework-style unfused step: every layer's dW is produced by the
+    # backward pass and alive until the optimizer runs over all of them (measured as the peak
+    # memory above what the fused block holds)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    grads = []
+    for i, d in enumerate(layers):
+        forge.dgrad(d["dY"], d["W"], d["dX"])
+        grads.append(torch.empty((d["N"], d["K"]), dtype=torch.float32, device="cuda"))
+        forge.wgrad_gemm(d["X"], d["dY"], grads[-1])
+    for i, d in enumerate(layers):
+        forge.optimizer_step(grads[i], d["W"], d["m"], d["v"], opt="adamw", hyper=w.hyper, step=2 * reps + 10,
+                             seed=synth.sr_seed(3, i))
+    torch.cuda.synchronize()
+    all_grads_extra = torch.cuda.max_memory_allocated() - base
+    del grads
     out["llama8b_block_T8192_dgrad_plus_step"] = {
         "block_us": pctl(block), "tflops_wgrad_plus_dgrad": round(flop / (b50 * 1e-6) / 1e12, 1),
         "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)},
-        "unfused_block_us": pctl(ub)}
+        "unfused_block_us": pctl(ub), "unfused_all_gradients_peak_extra_bytes": int(all_grads_extra),
+        "fused_peak_extra_bytes": int(fused_extra)}
     del layers
     return out
 

@@ -28,7 +28,7 @@ __device__ __forceinline__ float input_scale(const GemmArgs& g) {
 // bf16 inputs, 256 x 128 workgroup tiles fed by LDS DMA (forge_mainloop2.h): 32-token slabs,
 // three in LDS (72 KiB), so two workgroups share a CU and each SIMD runs two waves.  The
 // launcher may turn the last k-block columns into 128 x 128 half tiles (four 32-token slabs in
-// LDS) so that the last round of workgroups fills the chip (see plan_split).
+// LDS) so that the last round of workgroups fills the chip (plan::plan_split, forge_plan.h).
 using Pipe2 = ml2::Pipe<32, 3>;
 using Pipe2H = ml2::Pipe<32, 4, 4>;
 constexpr int kOcc2 = 2;

@@ -11,12 +11,14 @@
 
 namespace forge {
 
+static_assert(ml2::BM == plan::kRows && ml2::BN == plan::kCols && ml2::BM_HALF == plan::kHalfRows,
+              "the launch plans and the kernels use the same tiles");
+
 // Full 256 x 128 tile: contraction, then the epilogue over its two 128-row halves.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
-  int nb, kb;
-  tile_coords_at(b, g.nbn, g.kb_split, nb, kb);
-  const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  int n0, k0;
+  plan::full_tile(g, b, n0, k0);
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
@@ -26,9 +28,8 @@ __device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs
 // Half 128 x 128 tile hb of the blocks [kb_split, nbk): all 128 rows staged at once.
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
-  int nb, kb;
-  tile_coords_at(hb, 2 * g.nbn, g.nbk - g.kb_split, nb, kb);
-  const int n0 = g.nb_base * ml2::BM + nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
+  int n0, k0;
+  plan::half_tile(g, hb, n0, k0);
   ml2::floatx4 acc[4][4];
   ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
   float* st = reinterpret_cast<float*>(smem);
@@ -55,10 +56,9 @@ static_assert(kSmemW <= 160 * 1024, "wide tiles fit the CU's LDS");
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel2w(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemW];
-  int nb, kb;
-  tile_coords_at((int)blockIdx.x, g.nbn, g.nbk / 2, nb, kb);
+  int n0, kw0;
+  plan::wide_tile(g, (int)blockIdx.x, n0, kw0);
   const int kh = (int)(threadIdx.x >> 8);
-  const int n0 = (g.nb_base + nb) * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
   ml2::floatx4 acc[8][4];
   ml2::contract_wide(acc, smem, g, n0, kw0);
   unsigned char* mine = smem + kh * ml2::EPI_BYTES;

@@ -20,9 +20,8 @@ static_assert(ml8::SMEM <= kSmem2, "fp8 stages fit the shared buffer size");
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel8(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
-  int nb, kb;
-  tile_coords(g.nbn, g.nbk, nb, kb);
-  const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  int n0, k0;
+  plan::tile8(g, (int)blockIdx.x, n0, k0);
   ml8::floatx16 acc[4][2];
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
@@ -38,10 +37,9 @@ static_assert(kSmem8W <= 160 * 1024, "wide fp8 tiles fit the CU's LDS");
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel8w(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem8W];
-  int nb, kb;
-  tile_coords_at((int)blockIdx.x, g.nbn, g.nbk / 2, nb, kb);
+  int n0, kw0;
+  plan::wide_tile(g, (int)blockIdx.x, n0, kw0);
   const int kh = (int)(threadIdx.x >> 8);
-  const int n0 = (g.nb_base + nb) * ml2::BM, kw0 = (g.kb_base + 2 * kb) * ml2::BN;
   ml8::floatx16 acc[4][2];
   ml8::contract_wide(acc, smem, g, n0, kw0);
   const float scale = g.dy_scale[0] * g.x_scale[0];

@@ -60,10 +60,9 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
   float* st = reinterpret_cast<float*>(smem);
   const int b = (int)blockIdx.x;
-  int nb, kb;
+  int n0, k0;
   if (b < g.nfull) {
-    tile_coords_at(b, g.nbn, g.kb_split, nb, kb);
-    const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+    plan::full_tile(g, b, n0, k0);
     ml2::floatx4 acc[8][4];
     ml2::contract<Pipe2>(acc, smem, g, n0, k0);
 #pragma unroll 1
@@ -74,8 +73,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
       __syncthreads();
     }
   } else {
-    tile_coords_at(b - g.nfull, 2 * g.nbn, g.nbk - g.kb_split, nb, kb);
-    const int n0 = g.nb_base * ml2::BM + nb * ml2::BM_HALF, k0 = (g.kb_base + g.kb_split + kb) * ml2::BN;
+    plan::half_tile(g, b - g.nfull, n0, k0);
     ml2::floatx4 acc[4][4];
     ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
     ml2::stage_acc_all(st, acc, 1.0f);
@@ -86,9 +84,8 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel2(GemmAr
 
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmArgs g, float* dW) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem2];
-  int nb, kb;
-  tile_coords(g.nbn, g.nbk, nb, kb);
-  const int n0 = (g.nb_base + nb) * ml2::BM, k0 = (g.kb_base + kb) * ml2::BN;
+  int n0, k0;
+  plan::tile8(g, (int)blockIdx.x, n0, k0);
   ml8::floatx16 acc[4][2];
   ml8::contract(acc, smem, g, n0, k0);
   const float scale = g.dy_scale[0] * g.x_scale[0];
@@ -113,93 +110,6 @@ static int slots_on_current_device() {
     cached[dev] = 2 * cu;
   }
   return cached[dev];
-}
-
-// Tile plan of the 256 x 128 path.  With F full tiles and S workgroup slots, the last round
-// holds F mod S tiles and leaves CUs with one workgroup; turning the last c k-block columns
-// into 128 x 128 half tiles (c = the fewest columns that hold that remainder) ends the launch
-// with a round of half tiles instead.  Returns the grid size.
-static unsigned plan_split(GemmArgs& g) {
-  const int nbN = g.nbn, nbK = g.nbk;
-  const int full = nbN * nbK, slots = slots_on_current_device();
-  const int rem = full % slots;
-  const int c = rem == 0 ? 0 : std::min(nbK, (rem + nbN - 1) / nbN);
-  g.kb_split = nbK - c;
-  g.nfull = nbN * g.kb_split;
-  return (unsigned)(g.nfull + 2 * nbN * c);
-}
-
-// Wide 256 x 256 tiles for long token counts (T >= 8192, where the faster contraction outweighs
-// the epilogue that no other workgroup on the CU overlaps; at T = 4096 both layouts take the same
-// time), in whole rounds of one workgroup per CU.  Either the first kw 256-column blocks of every
-// 256-row block, kw the largest count for which N / 256 * kw is a positive multiple of the CU
-// count, or, where no column count works and K is a multiple of 256, the first nw 256-row blocks
-// over all columns, nw the largest such count of rows.  The rest of the weight runs on the
-// 256 x 128 path.
-struct WidePlan {
-  int kw = 0, nw = 0;
-};
-
-static WidePlan plan_wide(const GemmArgs& g) {
-  WidePlan p;
-  if (g.T < 8192) return p;
-  const int nbN = (int)(g.N / ml2::BM), nbK2 = (int)(g.K / (2 * ml2::BN)), cus = slots_on_current_device() / 2;
-  for (int kw = nbK2; kw > 0; --kw)
-    if ((nbN * kw) % cus == 0) {
-      p.kw = kw;
-      return p;
-    }
-  if (g.K % (2 * ml2::BN) == 0)  // rows of wide tiles span every column
-    for (int nw = nbN; nw > 0; --nw)
-      if ((nw * nbK2) % cus == 0) {
-        p.nw = nw;
-        return p;
-      }
-  return p;
-}
-
-// The launch of a wide plan: the region of the wide tiles (g.nb_base, nbn, kb_base, nbk) and the
-// region left to the 256 x 128 path (rest; nbn or nbk 0 when nothing is left).
-static void split_wide(const GemmArgs& g, const WidePlan& p, GemmArgs& wide, GemmArgs& rest) {
-  const int nbN = (int)(g.N / ml2::BM), nbK = (int)(g.K / ml2::BN);
-  wide = g;
-  rest = g;
-  wide.nb_base = rest.nb_base = 0;
-  wide.kb_base = rest.kb_base = 0;
-  if (p.kw > 0) {
-    wide.nbn = nbN;
-    wide.nbk = 2 * p.kw;
-    rest.nbn = nbN;
-    rest.kb_base = 2 * p.kw;
-    rest.nbk = nbK - 2 * p.kw;
-  } else {
-    wide.nbn = p.nw;
-    wide.nbk = nbK;
-    rest.nb_base = p.nw;
-    rest.nbn = nbN - p.nw;
-    rest.nbk = nbK;
-  }
-}
-
-// The region of a whole weight on the LDS-DMA paths: every 256-row and 128-column block.
-static GemmArgs whole_dma(const GemmArgs& g) {
-  GemmArgs r = g;
-  r.nb_base = 0;
-  r.nbn = (int)(g.N / ml2::BM);
-  r.kb_base = 0;
-  r.nbk = (int)(g.K / ml2::BN);
-  return r;
-}
-
-// The 256 x 128 path needs N % 256 == 0 and at least 128 of its tiles (256 workgroups once the
-// plan turns them into half tiles).
-static bool use_v2(int in_type, const GemmArgs& g) {
-  return in_type == FORGE_IN_BF16 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 128;
-}
-
-// fp8 inputs: the DMA path needs N % 256 == 0 and at least 256 of its tiles.
-static bool use_v8(int in_type, const GemmArgs& g) {
-  return in_type == FORGE_IN_FP8 && g.N % ml2::BM == 0 && (g.N / ml2::BM) * (g.K / ml2::BN) >= 256;
 }
 
 // Element-wise rule over a materialised gradient, in the layout of the fused epilogue for the
@@ -359,79 +269,54 @@ static FusedFn fused8_for(int s_type, int wide, int w_type, int opt) {
 
 int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmArgs& g, const EpiArgs& e,
                       void* stream) {
-  FusedFn fn = nullptr;
-  if (use_v2(in_type, g)) {
-    fn = fused2_for(s_type, 0, w_type, opt);
-    FusedFn fw = fused2_for(s_type, 1, w_type, opt);
-    if (!fn || !fw) return (int)hipErrorInvalidValue;
-    GemmArgs g2 = whole_dma(g);
-    // wide tiles first; the columns or rows they leave go to the 256 x 128 path in a second launch
-    const WidePlan wp = plan_wide(g);
-    if (wp.kw > 0 || wp.nw > 0) {
-      GemmArgs gw;
-      split_wide(g, wp, gw, g2);
-      const unsigned gridw = (unsigned)(gw.nbn * (gw.nbk / 2));
-      hipLaunchKernelGGL(fw, dim3(gridw), dim3(2 * ml2::THREADS), 0, (hipStream_t)stream, gw, e);
-      const hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return (int)err;
-      if (g2.nbn == 0 || g2.nbk == 0) return (int)hipSuccess;
+  plan::Launch L[2];
+  const int n = plan::plan_launches(in_type, g, slots_on_current_device() / 2, 1, L);
+  for (int i = 0; i < n; ++i) {
+    FusedFn fn = nullptr;
+    unsigned threads = ml2::THREADS;
+    if (L[i].kind == plan::LAUNCH_WIDE) {
+      fn = in_type == FORGE_IN_BF16 ? fused2_for(s_type, 1, w_type, opt) : fused8_for(s_type, 1, w_type, opt);
+      threads = 2 * ml2::THREADS;
+    } else if (L[i].kind == plan::LAUNCH_V2) {
+      fn = fused2_for(s_type, 0, w_type, opt);
+    } else if (L[i].kind == plan::LAUNCH_V8) {
+      fn = fused8_for(s_type, 0, w_type, opt);
+    } else {
+      if (in_type == FORGE_IN_BF16) fn = select_fused1<FORGE_IN_BF16>(w_type, s_type, opt);
+      else if (in_type == FORGE_IN_F32) fn = select_fused1<FORGE_IN_F32>(w_type, s_type, opt);
+      else if (in_type == FORGE_IN_FP8) fn = select_fused1<FORGE_IN_FP8>(w_type, s_type, opt);
+      threads = kThreads;
     }
-    const unsigned grid2 = plan_split(g2);
-    hipLaunchKernelGGL(fn, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, e);
-    return (int)hipGetLastError();
+    if (!fn) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(L[i].grid), dim3(threads), 0, (hipStream_t)stream, L[i].g, e);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return (int)err;
   }
-  if (use_v8(in_type, g)) {
-    fn = fused8_for(s_type, 0, w_type, opt);
-    FusedFn fw = fused8_for(s_type, 1, w_type, opt);
-    if (!fn || !fw) return (int)hipErrorInvalidValue;
-    GemmArgs g8 = whole_dma(g);
-    // wide tiles first (same rule as for bf16 inputs); the rest on 256 x 128 tiles
-    const WidePlan wp = plan_wide(g);
-    if (wp.kw > 0 || wp.nw > 0) {
-      GemmArgs gw;
-      split_wide(g, wp, gw, g8);
-      const unsigned gridw = (unsigned)(gw.nbn * (gw.nbk / 2));
-      hipLaunchKernelGGL(fw, dim3(gridw), dim3(2 * ml2::THREADS), 0, (hipStream_t)stream, gw, e);
-      const hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return (int)err;
-      if (g8.nbn == 0 || g8.nbk == 0) return (int)hipSuccess;
-    }
-    const unsigned grid8 = (unsigned)(g8.nbn * g8.nbk);
-    hipLaunchKernelGGL(fn, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g8, e);
-    return (int)hipGetLastError();
-  }
-  if (in_type == FORGE_IN_BF16) fn = select_fused1<FORGE_IN_BF16>(w_type, s_type, opt);
-  else if (in_type == FORGE_IN_F32) fn = select_fused1<FORGE_IN_F32>(w_type, s_type, opt);
-  else if (in_type == FORGE_IN_FP8) fn = select_fused1<FORGE_IN_FP8>(w_type, s_type, opt);
-  if (!fn) return (int)hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, e);
-  return (int)hipGetLastError();
+  return (int)hipSuccess;
 }
 
 int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
-  if (use_v2(in_type, g)) {
-    GemmArgs g2 = whole_dma(g);
-    const unsigned grid2 = plan_split(g2);
-    hipLaunchKernelGGL(wgrad_gemm_kernel2, dim3(grid2), dim3(ml2::THREADS), 0, (hipStream_t)stream, g2, dW);
-    return (int)hipGetLastError();
+  plan::Launch L[2];
+  const int n = plan::plan_launches(in_type, g, slots_on_current_device() / 2, 0, L);
+  for (int i = 0; i < n; ++i) {
+    const GemmArgs& gl = L[i].g;
+    const dim3 grid(L[i].grid);
+    if (L[i].kind == plan::LAUNCH_V2)
+      hipLaunchKernelGGL(wgrad_gemm_kernel2, grid, dim3(ml2::THREADS), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_V8)
+      hipLaunchKernelGGL(wgrad_gemm_kernel8, grid, dim3(ml2::THREADS), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_BF16)
+      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_BF16>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_F32)
+      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_F32>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_FP8)
+      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_FP8>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else
+      return (int)hipErrorInvalidValue;
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return (int)err;
   }
-  if (use_v8(in_type, g)) {
-    const GemmArgs g8 = whole_dma(g);
-    const unsigned grid8 = (unsigned)(g8.nbn * g8.nbk);
-    hipLaunchKernelGGL(wgrad_gemm_kernel8, dim3(grid8), dim3(ml2::THREADS), 0, (hipStream_t)stream, g8, dW);
-    return (int)hipGetLastError();
-  }
-  const unsigned grid = (unsigned)((g.N / kBM) * (g.K / kBN));
-  if (in_type == FORGE_IN_BF16)
-    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_BF16>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
-  else if (in_type == FORGE_IN_F32)
-    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_F32>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
-  else if (in_type == FORGE_IN_FP8)
-    hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_FP8>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, g, dW);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  return (int)hipSuccess;
 }
 
 int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n_elem, const EpiArgs& e,

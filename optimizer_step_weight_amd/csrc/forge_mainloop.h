@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include "forge_device.h"
+#include "forge_plan.h"
 
 namespace forge {
 
@@ -59,22 +60,8 @@ struct InT<FORGE_IN_FP8> {
   static constexpr int ESZ = 1, TK = 128, RG = 16;
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each
-// with its own L2.  Give every XCD a contiguous run of tile ids, and inside a run walk the
-// tiles in groups of 4 n-blocks, so that concurrently running tiles share dY and X panels in
-// their XCD's L2.
-__device__ __forceinline__ void tile_coords_at(int b, int nbN, int nbK, int& nb, int& kb) {
-  const int nt = nbN * nbK;
-  const int per = nt >> 3, rem = nt & 7, x = b & 7, loc = b >> 3;
-  const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
-  constexpr int G = 4;
-  const int group = G * nbK;
-  const int gid = t / group, first = gid * G;
-  const int gsz = min(nbN - first, G);
-  const int r = t - gid * group;
-  nb = first + r % gsz;
-  kb = r / gsz;
-}
+// Workgroup -> tile mapping (XCD-aware; forge_plan.h).
+using plan::tile_coords_at;
 
 __device__ __forceinline__ void tile_coords(int nbN, int nbK, int& nb, int& kb) {
   tile_coords_at((int)blockIdx.x, nbN, nbK, nb, kb);

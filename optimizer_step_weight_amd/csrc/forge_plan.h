@@ -1,0 +1,174 @@
+// forge_plan.h -- how a weight is cut into workgroup tiles: the launch plans of the fused step
+// and the GEMM, and the tile each workgroup takes.  Host and device share this code (the
+// kernels map blockIdx to a tile with it, the launchers size their grids with it, and a host
+// test checks with it that every element of W is covered exactly once).
+//
+// FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism": one workgroup
+// accumulates whole tiles of W over all tokens; the tile shape does not change the result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "forge_internal.h"
+
+namespace forge {
+namespace plan {
+
+constexpr int kRows = 256;      // full tile rows (n) on the LDS-DMA paths
+constexpr int kCols = 128;      // tile columns (k); a wide tile spans two
+constexpr int kHalfRows = 128;  // half tile rows
+constexpr int kSmallTile = 128; // register-staged path: 128 x 128 tiles
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each
+// with its own L2.  Give every XCD a contiguous run of tile ids, and inside a run walk the
+// tiles in groups of 4 row blocks, so that concurrently running tiles share dY and X panels in
+// their XCD's L2.  Maps b in [0, nbN nbK) to (nb, kb) one to one.
+__host__ __device__ inline void tile_coords_at(int b, int nbN, int nbK, int& nb, int& kb) {
+  const int nt = nbN * nbK;
+  const int per = nt >> 3, rem = nt & 7, x = b & 7, loc = b >> 3;
+  const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
+  constexpr int G = 4;
+  const int group = G * nbK;
+  const int gid = t / group, first = gid * G;
+  const int gsz = (nbN - first) < G ? (nbN - first) : G;
+  const int r = t - gid * group;
+  nb = first + r % gsz;
+  kb = r / gsz;
+}
+
+// ---- tile origins, per kind of workgroup (row n0 and column k0 of its first element)
+// 256 x 128 tile b in [0, nfull) of a 256 x 128 launch (fused step or GEMM).
+__host__ __device__ inline void full_tile(const GemmArgs& g, int b, int& n0, int& k0) {
+  int nb, kb;
+  tile_coords_at(b, g.nbn, g.kb_split, nb, kb);
+  n0 = (g.nb_base + nb) * kRows;
+  k0 = (g.kb_base + kb) * kCols;
+}
+// 128 x 128 half tile hb (the workgroups after nfull) of a 256 x 128 launch.
+__host__ __device__ inline void half_tile(const GemmArgs& g, int hb, int& n0, int& k0) {
+  int nb, kb;
+  tile_coords_at(hb, 2 * g.nbn, g.nbk - g.kb_split, nb, kb);
+  n0 = g.nb_base * kRows + nb * kHalfRows;
+  k0 = (g.kb_base + g.kb_split + kb) * kCols;
+}
+// 256 x 256 tile b of a wide launch (columns k0 .. k0 + 255).
+__host__ __device__ inline void wide_tile(const GemmArgs& g, int b, int& n0, int& k0) {
+  int nb, kb;
+  tile_coords_at(b, g.nbn, g.nbk / 2, nb, kb);
+  n0 = (g.nb_base + nb) * kRows;
+  k0 = (g.kb_base + 2 * kb) * kCols;
+}
+// 256 x 128 tile b of an fp8 launch (no half tiles).
+__host__ __device__ inline void tile8(const GemmArgs& g, int b, int& n0, int& k0) {
+  int nb, kb;
+  tile_coords_at(b, g.nbn, g.nbk, nb, kb);
+  n0 = (g.nb_base + nb) * kRows;
+  k0 = (g.kb_base + kb) * kCols;
+}
+
+// ---- launch plans (host)
+// The region of a whole weight on the LDS-DMA paths: every 256-row and 128-column block.
+inline GemmArgs whole_dma(const GemmArgs& g) {
+  GemmArgs r = g;
+  r.nb_base = 0;
+  r.nbn = (int)(g.N / kRows);
+  r.kb_base = 0;
+  r.nbk = (int)(g.K / kCols);
+  return r;
+}
+
+// 256 x 128 path with half tiles.  With F full tiles and S workgroup slots, the last round
+// holds F mod S tiles and leaves CUs with one workgroup; turning the last c column blocks into
+// 128 x 128 half tiles (c = the fewest columns that hold that remainder) ends the launch with a
+// round of half tiles instead.  Sets nfull and kb_split; returns the grid size.
+inline unsigned plan_split(GemmArgs& g, int slots) {
+  const int nbN = g.nbn, nbK = g.nbk;
+  const int full = nbN * nbK;
+  const int rem = full % slots;
+  const int c0 = rem == 0 ? 0 : (rem + nbN - 1) / nbN;
+  const int c = c0 < nbK ? c0 : nbK;
+  g.kb_split = nbK - c;
+  g.nfull = nbN * g.kb_split;
+  return (unsigned)(g.nfull + 2 * nbN * c);
+}
+
+// Wide 256 x 256 tiles for long token counts (T >= 8192, where the faster contraction outweighs
+// the epilogue that no other workgroup on the CU overlaps; at T = 4096 both layouts take the same
+// time), in whole rounds of one workgroup per CU.  Either the first kw 256-column blocks of every
+// 256-row block, kw the largest count for which N / 256 * kw is a positive multiple of the CU
+// count, or, where no column count works and K is a multiple of 256, the first nw 256-row blocks
+// over all columns, nw the largest such count of rows.  The rest of the weight runs on the
+// 256 x 128 path.
+struct WidePlan {
+  int kw = 0, nw = 0;
+};
+
+inline WidePlan plan_wide(const GemmArgs& g, int cus) {
+  WidePlan p;
+  if (g.T < 8192 || cus <= 0) return p;
+  const int nbN = (int)(g.N / kRows), nbK2 = (int)(g.K / (2 * kCols));
+  for (int kw = nbK2; kw > 0; --kw)
+    if ((nbN * kw) % cus == 0) {
+      p.kw = kw;
+      return p;
+    }
+  if (g.K % (2 * kCols) == 0)  // rows of wide tiles span every column
+    for (int nw = nbN; nw > 0; --nw)
+      if ((nw * nbK2) % cus == 0) {
+        p.nw = nw;
+        return p;
+      }
+  return p;
+}
+
+// The 256 x 128 path needs N % 256 == 0 and at least 128 of its tiles (256 workgroups once the
+// plan turns them into half tiles); fp8 inputs at least 256 tiles.
+inline bool use_v2(int in_type, const GemmArgs& g) {
+  return in_type == FORGE_IN_BF16 && g.N % kRows == 0 && (g.N / kRows) * (g.K / kCols) >= 128;
+}
+inline bool use_v8(int in_type, const GemmArgs& g) {
+  return in_type == FORGE_IN_FP8 && g.N % kRows == 0 && (g.N / kRows) * (g.K / kCols) >= 256;
+}
+
+// One kernel launch of a plan.
+enum : int { LAUNCH_WIDE = 0, LAUNCH_V2 = 1, LAUNCH_V8 = 2, LAUNCH_SMALL = 3 };
+struct Launch {
+  int kind;
+  GemmArgs g;
+  unsigned grid;  // workgroups
+};
+
+// The launches of the fused step (fused = 1) or of the GEMM (fused = 0) for inputs of type
+// in_type on a device with `cus` compute units (two workgroup slots each on the 256 x 128
+// path): wide tiles first where they apply (fused step only), then the rest.  Returns the
+// number of launches (0 to 2).
+inline int plan_launches(int in_type, const GemmArgs& g, int cus, int fused, Launch (&out)[2]) {
+  int n = 0;
+  if (use_v2(in_type, g) || use_v8(in_type, g)) {
+    const int kind = use_v2(in_type, g) ? LAUNCH_V2 : LAUNCH_V8;
+    GemmArgs rest = whole_dma(g);
+    const WidePlan wp = fused ? plan_wide(g, cus) : WidePlan{};
+    if (wp.kw > 0 || wp.nw > 0) {
+      GemmArgs wide = rest;
+      if (wp.kw > 0) {
+        wide.nbk = 2 * wp.kw;
+        rest.kb_base = 2 * wp.kw;
+        rest.nbk -= 2 * wp.kw;
+      } else {
+        wide.nbn = wp.nw;
+        rest.nb_base = wp.nw;
+        rest.nbn -= wp.nw;
+      }
+      out[n++] = Launch{LAUNCH_WIDE, wide, (unsigned)(wide.nbn * (wide.nbk / 2))};
+      if (rest.nbn == 0 || rest.nbk == 0) return n;
+    }
+    const unsigned grid = kind == LAUNCH_V2 ? plan_split(rest, 2 * cus) : (unsigned)(rest.nbn * rest.nbk);
+    out[n++] = Launch{kind, rest, grid};
+    return n;
+  }
+  out[n++] = Launch{LAUNCH_SMALL, g, (unsigned)((g.N / kSmallTile) * (g.K / kSmallTile))};
+  return n;
+}
+
+}  // namespace plan
+}  // namespace forge
