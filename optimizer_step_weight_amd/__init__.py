@@ -193,9 +193,11 @@ def wgrad_step(X, dY, W, m=None, v=None, *, opt="adamw", hyper=None, step: int, 
     (int8 m, uint8 v with block scales) use the linear absmax map, or the dynamic map with
     state_map="dynamic"."""
     o = _opts(w_preround_out, sr, W)
+    dyn = _dyn(state_map)
     _check(_lib().forge_wgrad_step(_ref(_tensor(X, x_scale)), _ref(_tensor(dY, dy_scale)), _ref(_tensor(W)),
-                                   _ref(_tensor(m, m_scale, _dyn(state_map))), _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)),
-                                   _opt(opt), int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+                                   _ref(_tensor(m, m_scale, dyn)), _ref(_tensor(v, v_scale, dyn)),
+                                   ctypes.byref(_hyper(hyper)), _opt(opt), int(step), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                   _ref(o), _stream(stream)))
 
 
 def dgrad(dY, W, dX, *, stream=None):
@@ -207,9 +209,10 @@ def linear_backward_step(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=Non
                          m_scale=None, v_scale=None, w_preround_out=None, sr=True, state_map="linear", stream=None):
     """dgrad then the fused step, in that order (forge_linear_backward_step)."""
     o = _opts(w_preround_out, sr, W)
+    dyn = _dyn(state_map)
     _check(_lib().forge_linear_backward_step(
-        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, _dyn(state_map))),
-        _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, dyn)),
+        _ref(_tensor(v, v_scale, dyn)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 
@@ -223,9 +226,10 @@ def optimizer_step(dW, W, m=None, v=None, *, opt="adamw", hyper=None, step: int,
                    v_scale=None, w_preround_out=None, sr=True, state_map="linear", stream=None):
     """Unfused phase 2: the rule applied to a materialised gradient (forge_optimizer_step)."""
     o = _opts(w_preround_out, sr, W)
-    _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale, _dyn(state_map))),
-                                       _ref(_tensor(v, v_scale, _dyn(state_map))), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
-                                       int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+    dyn = _dyn(state_map)
+    _check(_lib().forge_optimizer_step(_ref(_tensor(dW)), _ref(_tensor(W)), _ref(_tensor(m, m_scale, dyn)),
+                                       _ref(_tensor(v, v_scale, dyn)), ctypes.byref(_hyper(hyper)), _opt(opt),
+                                       int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 
 def step_scalars(opt, hyper, step: int) -> dict:
