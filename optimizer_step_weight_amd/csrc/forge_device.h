@@ -11,6 +11,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "forge_internal.h"
 
 namespace forge {
@@ -134,6 +137,20 @@ struct RuleStates {
   static constexpr bool v = OPT == FORGE_OPT_ADAMW || OPT == FORGE_OPT_NADAM || OPT == FORGE_OPT_RADAM ||
                             OPT == FORGE_OPT_RMSPROP || OPT == FORGE_OPT_ADAGRAD;
 };
+
+// ------------------------------------------------------------------ compile-time loops
+// f(std::integral_constant<int, i>) for i = 0 .. N-1.  Register arrays indexed by a loop
+// counter stay in registers only if the loop is unrolled; the compiler declines to unroll the
+// large epilogue loops (the dynamic 8-bit map makes their bodies long) and would then move such
+// arrays to scratch memory, so these loops take their index as a constant.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ------------------------------------------------------------------ vector memory helpers
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

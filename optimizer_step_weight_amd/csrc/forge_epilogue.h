@@ -58,11 +58,6 @@ __device__ __forceinline__ void staged_grad(const float* st, int s, float (&gr)[
   }
 }
 
-// Full 256 x 128 tile.  Epilogue: the gradient goes through LDS in two 128-row halves; each
-// thread owns 4 segments of 16 elements per half.  The stored state of the next two segments
-// is in flight while the current one is updated (the first loads leave before the staging);
-// in the first half the other half's accumulators are still live, so unless DEEP0 only one
-// segment is in flight there (bf16 weights with fp32 moments on the bf16 path use two).
 // ---- epilogue in the lane-contiguous unit layout (forge_device.h, "one 4-element unit")
 // 128 staged rows are 16 rounds of 8 rows: in round rho this thread's unit is row
 // 8 rho + 2 wave + lane / 32, columns 4 (lane % 32) .. +3, so a wave touches two contiguous row
@@ -127,8 +122,8 @@ __device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& 
     unit_batch_apply<OPT, WT, ST>(cur, w, st, g, e, rows0, k0, b);
   };
   unit_batch_load<OPT, WT, ST>(xa, g, e, n0, k0, 0);
-#pragma unroll
-  for (int h = 0; h < HALVES; ++h) {
+  static_for<HALVES>([&](auto hc) {  // the staging of half h reads accumulators chosen by h
+    constexpr int h = decltype(hc)::value;
     stage(h);
     __syncthreads();
     batch(xa, xb, h, 0);
@@ -136,7 +131,7 @@ __device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& 
     batch(xa, xb, h, 2);
     batch(xb, xa, h, 3);
     __syncthreads();
-  }
+  });
 }
 
 // Segment epilogue: 16 consecutive elements of a row per thread (4 per 128-row half).  Used
@@ -147,6 +142,11 @@ __device__ __forceinline__ void unit_epilogue(const GemmArgs& g, const EpiArgs& 
 // updated, so its latency hides behind that update.  fp32 weights and Lion keep one segment
 // in flight (loaded after the update), which their registers allow without spilling.  The
 // first segment's loads leave before the staging.
+template <int OPT, int WT, int ST>
+constexpr bool seg_ahead() {
+  return WT == FORGE_W_BF16 && OPT != FORGE_OPT_LION;
+}
+
 template <int OPT, int WT, int ST, int HALVES, class Stage>
 __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
                                              int k0, Stage&& stage) {
@@ -156,17 +156,17 @@ __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e
     seg_pos(j & 3, row, kseg);
     return (uint32_t)(n0 + (j >> 2) * ml2::EPI_ROWS + row) * (uint32_t)g.K + (uint32_t)(k0 + kseg * 16);
   };
-  constexpr bool AHEAD = WT == FORGE_W_BF16 && OPT != FORGE_OPT_LION;
+  constexpr bool AHEAD = seg_ahead<OPT, WT, ST>();
   SegIn xs[AHEAD ? 2 : 1];
   seg_load<OPT, WT, ST>(xs[0], index_of(0), e);
-#pragma unroll
-  for (int h = 0; h < HALVES; ++h) {
+  static_for<HALVES>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
     stage(h);
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int j = 4 * h + s;
-      const bool more = j + 1 < 4 * HALVES;
+    static_for<4>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int j = 4 * h + s;
+      constexpr bool more = j + 1 < 4 * HALVES;
       float gr[16];
       if constexpr (AHEAD) {
         if (more) seg_load<OPT, WT, ST>(xs[(j + 1) & 1], index_of(j + 1), e);
@@ -177,9 +177,9 @@ __device__ __forceinline__ void seg_epilogue(const GemmArgs& g, const EpiArgs& e
         seg_apply<OPT, WT, ST>(gr, index_of(j), xs[0], e);
         if (more) seg_load<OPT, WT, ST>(xs[0], index_of(j + 1), e);
       }
-    }
+    });
     __syncthreads();
-  }
+  });
 }
 
 // The epilogue for the state format: 4-element units for fp32 moments, segments for int8

@@ -2,5 +2,5 @@
 #include "forge_fused1.h"
 
 namespace forge {
-template FusedFn select_fused1<FORGE_IN_BF16>(int, int, int);
+template FusedFn select_fused1<FORGE_IN_BF16>(int, int, int, int);
 }  // namespace forge

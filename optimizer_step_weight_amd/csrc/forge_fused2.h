@@ -14,26 +14,43 @@ namespace forge {
 static_assert(ml2::BM == plan::kRows && ml2::BN == plan::kCols && ml2::BM_HALF == plan::kHalfRows,
               "the launch plans and the kernels use the same tiles");
 
-// Full 256 x 128 tile: contraction, then the epilogue over its two 128-row halves.
-template <int WT, int ST, int OPT>
-__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
-  int n0, k0;
-  plan::full_tile(g, b, n0, k0);
+// Full 256 x 128 tile at (n0, k0): contraction, then the epilogue over its two 128-row halves.
+// before_update() runs between the two (the one-launch backward step waits there until no
+// dgrad tile still reads this tile's old weight).
+template <int WT, int ST, int OPT, class BeforeUpdate>
+__device__ __forceinline__ void fused_full_tile_at(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                                   int k0, BeforeUpdate&& before_update) {
   ml2::floatx4 acc[8][4];
   ml2::contract<Pipe2>(acc, smem, g, n0, k0);
+  if (!before_update()) return;
   float* st = reinterpret_cast<float*>(smem);
   tile_epilogue<OPT, WT, ST, 2, true>(g, e, smem, n0, k0, [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
 }
 
-// Half 128 x 128 tile hb of the blocks [kb_split, nbk): all 128 rows staged at once.
+// Half 128 x 128 tile at (n0, k0): all 128 rows staged at once.
+template <int WT, int ST, int OPT, class BeforeUpdate>
+__device__ __forceinline__ void fused_half_tile_at(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int n0,
+                                                   int k0, BeforeUpdate&& before_update) {
+  ml2::floatx4 acc[4][4];
+  ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
+  if (!before_update()) return;
+  float* st = reinterpret_cast<float*>(smem);
+  tile_epilogue<OPT, WT, ST, 1, true>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
+}
+
+// Full tile b of the launch's full tiles [0, nfull), and half tile hb of the blocks
+// [kb_split, nbk).
+template <int WT, int ST, int OPT>
+__device__ __forceinline__ void fused_full_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int b) {
+  int n0, k0;
+  plan::full_tile(g, b, n0, k0);
+  fused_full_tile_at<WT, ST, OPT>(g, e, smem, n0, k0, [] { return true; });
+}
 template <int WT, int ST, int OPT>
 __device__ __forceinline__ void fused_half_tile(const GemmArgs& g, const EpiArgs& e, unsigned char* smem, int hb) {
   int n0, k0;
   plan::half_tile(g, hb, n0, k0);
-  ml2::floatx4 acc[4][4];
-  ml2::contract<Pipe2H>(acc, smem, g, n0, k0);
-  float* st = reinterpret_cast<float*>(smem);
-  tile_epilogue<OPT, WT, ST, 1, true>(g, e, smem, n0, k0, [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
+  fused_half_tile_at<WT, ST, OPT>(g, e, smem, n0, k0, [] { return true; });
 }
 
 template <int WT, int ST, int OPT>

@@ -27,30 +27,31 @@
 
 #include <algorithm>
 
-#include "forge_epilogue.h"
+#include "forge_dgrad.h"
 
 namespace forge {
 
-template <int IN>
-__global__ __launch_bounds__(kThreads, 2) void wgrad_gemm_kernel(GemmArgs g, float* dW) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
-  const int nbN = (int)(g.N / kBM), nbK = (int)(g.K / kBN);
+template <int IN, int S>
+__global__ __launch_bounds__(kThreads, S == 128 ? 2 : 4) void wgrad_gemm_kernel(GemmArgs g, float* dW) {
+  using TL = SmallTile<S>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[TL::SMEM];
+  const int nbN = (int)(g.N / S), nbK = (int)(g.K / S);
   int nb, kb;
   tile_coords(nbN, nbK, nb, kb);
-  const int n0 = nb * kBM, k0 = kb * kBN;
+  const int n0 = nb * S, k0 = kb * S;
 
-  floatx4 acc[4][4];
-  contract_tile<IN>(acc, smem, g, n0, k0);
+  floatx4 acc[TL::NB][TL::NB];
+  contract_tile<IN, S>(acc, smem, g, n0, k0);
 
   float* st = reinterpret_cast<float*>(smem);
-  stage_acc(st, acc, input_scale<IN>(g));
+  stage_acc<S>(st, acc, input_scale<IN>(g));
   __syncthreads();
-  const int tid = threadIdx.x;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int seg = tid + kThreads * s, row = seg >> 3, kseg = seg & 7;
-    const float* p = st + row * kEpiLd + kseg * 16;
-    float* d = dW + (int64_t)(n0 + row) * g.K + k0 + kseg * 16;
+  for (int s = 0; s < TL::SEGS; ++s) {
+    int row, col;
+    small_seg<S>(s, row, col);
+    const float* p = st + row * kEpiLd + col;
+    float* d = dW + (int64_t)(n0 + row) * g.K + k0 + col;
 #pragma unroll
     for (int q = 0; q < 4; ++q) st16(d + 4 * q, *reinterpret_cast<const u32x4*>(p + 4 * q));
   }
@@ -152,9 +153,8 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* dW, int64_t
   }
 }
 
-// dX[T, K] = dY[T, N] . W[N, K], bf16 in, fp32 accumulate, bf16 (nearest-even) out.
-// 256-token x 128-column tiles, the reduction over N in 32-wide slabs fed by LDS DMA
-// (forge_mainloop2.h, dgrad section); two workgroups per CU.
+// dX[T, K] = dY[T, N] . W[N, K] on 256-token x 128-column tiles (forge_dgrad.h), two
+// workgroups per CU.
 static_assert(ml2::DgradPipe::SMEM <= kSmem2, "dgrad stages fit the shared buffer size");
 __global__ __launch_bounds__(ml2::THREADS, kOcc2) void dgrad_kernel2(const uint16_t* dY, const uint16_t* W,
                                                                      uint16_t* dX, int64_t T, int64_t N, int64_t K) {
@@ -162,40 +162,10 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void dgrad_kernel2(const uint1
   const int nbT = (int)((T + ml2::BM - 1) / ml2::BM), nbK = (int)(K / ml2::BN);
   int tb, kb;
   tile_coords_at((int)blockIdx.x, nbT, nbK, tb, kb);
-  const int64_t t0 = (int64_t)tb * ml2::BM;
-  const int k0 = kb * ml2::BN;
-  ml2::floatx4 acc[8][4];
-  ml2::dgrad_contract(acc, smem, dY, W, T, N, K, t0, k0);
-  float* st = reinterpret_cast<float*>(smem);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    ml2::stage_acc_half(st, acc, 1.0f, half);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      int row, kseg;
-      seg_pos(s, row, kseg);
-      const int64_t t = t0 + half * ml2::EPI_ROWS + row;
-      if (t >= T) continue;
-      float gr[16];
-      staged_grad(st, s, gr);
-      u32x4 a, b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
-        b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
-      }
-      uint16_t* d = dX + t * K + k0 + kseg * 16;
-      st16(d, a);
-      st16(d + 8, b);
-    }
-    __syncthreads();
-  }
+  dgrad_tile(dY, W, dX, T, N, K, (int64_t)tb * ml2::BM, kb * ml2::BN, smem, [] {});
 }
 
-// dX tiles of 256 tokens x 256 columns, one workgroup of 8 waves per CU (forge_mainloop2.h, wide
-// dgrad tiles): both 128-column halves share the dY slab and 4 slabs fit in LDS.  Each half
-// stages its accumulators through its own LDS buffer and stores bf16 rows as dgrad_kernel2 does.
+// dX tiles of 256 tokens x 256 columns, one workgroup of 8 waves per CU (forge_dgrad.h).
 constexpr int kSmemDW =
     ml2::DgradWidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::DgradWidePipe::SMEM : 2 * ml2::EPI_BYTES;
 static_assert(kSmemDW <= 160 * 1024, "wide dgrad tiles fit the CU's LDS");
@@ -206,36 +176,7 @@ __global__ __launch_bounds__(2 * ml2::THREADS, 1) void dgrad_kernel2w(const uint
   const int nbT = (int)((T + ml2::BM - 1) / ml2::BM), nbK2 = (int)(K / (2 * ml2::BN));
   int tb, kb;
   tile_coords_at((int)blockIdx.x, nbT, nbK2, tb, kb);
-  const int64_t t0 = (int64_t)tb * ml2::BM;
-  const int kh = (int)(threadIdx.x >> 8);
-  const int k0 = (2 * kb + kh) * ml2::BN;
-  ml2::floatx4 acc[8][4];
-  ml2::dgrad_wide_contract(acc, smem, dY, W, T, N, K, t0, 2 * kb * ml2::BN);
-  float* st = reinterpret_cast<float*>(smem + kh * ml2::EPI_BYTES);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    ml2::stage_acc_half(st, acc, 1.0f, half);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      int row, kseg;
-      seg_pos(s, row, kseg);
-      const int64_t t = t0 + half * ml2::EPI_ROWS + row;
-      if (t >= T) continue;
-      float gr[16];
-      staged_grad(st, s, gr);
-      u32x4 a, b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = f32_to_bf16_rne(gr[2 * q]) | (f32_to_bf16_rne(gr[2 * q + 1]) << 16);
-        b[q] = f32_to_bf16_rne(gr[8 + 2 * q]) | (f32_to_bf16_rne(gr[8 + 2 * q + 1]) << 16);
-      }
-      uint16_t* d = dX + t * K + k0 + kseg * 16;
-      st16(d, a);
-      st16(d + 8, b);
-    }
-    __syncthreads();
-  }
+  dgrad_tile_wide(dY, W, dX, T, N, K, (int64_t)tb * ml2::BM, 2 * kb * ml2::BN, smem);
 }
 
 // ------------------------------------------------------------------ dispatch tables
@@ -282,9 +223,10 @@ int launch_fused_step(int in_type, int w_type, int s_type, int opt, const GemmAr
     } else if (L[i].kind == plan::LAUNCH_V8) {
       fn = fused8_for(s_type, 0, w_type, opt);
     } else {
-      if (in_type == FORGE_IN_BF16) fn = select_fused1<FORGE_IN_BF16>(w_type, s_type, opt);
-      else if (in_type == FORGE_IN_F32) fn = select_fused1<FORGE_IN_F32>(w_type, s_type, opt);
-      else if (in_type == FORGE_IN_FP8) fn = select_fused1<FORGE_IN_FP8>(w_type, s_type, opt);
+      const int tile = L[i].tile;
+      if (in_type == FORGE_IN_BF16) fn = select_fused1<FORGE_IN_BF16>(w_type, s_type, opt, tile);
+      else if (in_type == FORGE_IN_F32) fn = select_fused1<FORGE_IN_F32>(w_type, s_type, opt, tile);
+      else if (in_type == FORGE_IN_FP8) fn = select_fused1<FORGE_IN_FP8>(w_type, s_type, opt, tile);
       threads = kThreads;
     }
     if (!fn) return (int)hipErrorInvalidValue;
@@ -305,12 +247,14 @@ int launch_wgrad_gemm(int in_type, const GemmArgs& g, float* dW, void* stream) {
       hipLaunchKernelGGL(wgrad_gemm_kernel2, grid, dim3(ml2::THREADS), 0, (hipStream_t)stream, gl, dW);
     else if (L[i].kind == plan::LAUNCH_V8)
       hipLaunchKernelGGL(wgrad_gemm_kernel8, grid, dim3(ml2::THREADS), 0, (hipStream_t)stream, gl, dW);
-    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_BF16)
-      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_BF16>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
-    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_F32)
-      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_F32>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
-    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_FP8)
-      hipLaunchKernelGGL(wgrad_gemm_kernel<FORGE_IN_FP8>, grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_BF16 && L[i].tile == 128)
+      hipLaunchKernelGGL((wgrad_gemm_kernel<FORGE_IN_BF16, 128>), grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_F32 && L[i].tile == 128)
+      hipLaunchKernelGGL((wgrad_gemm_kernel<FORGE_IN_F32, 128>), grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_F32 && L[i].tile == 64)
+      hipLaunchKernelGGL((wgrad_gemm_kernel<FORGE_IN_F32, 64>), grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
+    else if (L[i].kind == plan::LAUNCH_SMALL && in_type == FORGE_IN_FP8 && L[i].tile == 128)
+      hipLaunchKernelGGL((wgrad_gemm_kernel<FORGE_IN_FP8, 128>), grid, dim3(kThreads), 0, (hipStream_t)stream, gl, dW);
     else
       return (int)hipErrorInvalidValue;
     const hipError_t err = hipGetLastError();

@@ -34,14 +34,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 128;          // tile rows (n)
-constexpr int kBN = 128;          // tile cols (k)
 constexpr int kThreads = 256;
 constexpr int kLdsRow = 144;      // bytes per LDS panel row: 128 bytes of tokens + 16 pad
-constexpr int kPanel = 128 * kLdsRow;
-constexpr int kStage = 2 * kPanel;  // dY panel + X panel
-constexpr int kSmem = 2 * kStage;   // double buffered: 73728 bytes
-constexpr int kEpiLd = kBN + 4;     // fp32 staging row stride (floats) for the epilogue
+constexpr int kEpiLd = 128 + 4;   // fp32 staging row stride (floats) for the epilogue
+
+// Square tiles of side S (128, or 64 for layers too small to fill the chip): four waves, each
+// a (S / 2) x (S / 2) quadrant of NB x NB blocks of 16 x 16.
+template <int S>
+struct SmallTile {
+  static_assert(S == 128 || S == 64, "tile side");
+  static constexpr int NB = S / 32;
+  static constexpr int PANEL = S * kLdsRow;
+  static constexpr int STAGE = 2 * PANEL;    // dY panel + X panel
+  static constexpr int SMEM = 2 * STAGE;     // double buffered: 73728 bytes for S = 128
+  static constexpr int SEGS = S * S / (kThreads * 16);  // 16-element segments per thread
+  static constexpr int SEGS_PER_ROW = S / 16;
+  static_assert(S * kEpiLd * 4 <= SMEM, "the staging fits the panels' LDS");
+};
+constexpr int kSmem = SmallTile<128>::SMEM;
 
 // Per input type: element size, tokens per slab (so that a panel row is 128 bytes),
 // and the number of 8-row groups a slab holds.
@@ -124,45 +134,46 @@ __device__ __forceinline__ void store_transposed(unsigned char* panel, const u32
   (void)ESZ;
 }
 
-// One slab of MFMAs for a 64 x 64 wave tile.  sA: dY panel rows (n), sB: X panel rows (k).
-template <int IN>
-__device__ __forceinline__ void mma_slab(floatx4 (&acc)[4][4], const unsigned char* sA, const unsigned char* sB,
+// One slab of MFMAs for a wave tile of NB x NB blocks of 16 x 16.  sA: dY panel rows (n), sB:
+// X panel rows (k).
+template <int IN, int NB>
+__device__ __forceinline__ void mma_slab(floatx4 (&acc)[NB][NB], const unsigned char* sA, const unsigned char* sB,
                                          int lane) {
   const int r16 = lane & 15, q = lane >> 4;
   if constexpr (IN == FORGE_IN_BF16) {
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
-      bf16x8 a[4], b[4];
+      bf16x8 a[NB], b[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NB; ++i) {
         a[i] = *reinterpret_cast<const bf16x8*>(sA + (16 * i + r16) * kLdsRow + kq * 64 + q * 16);
         b[i] = *reinterpret_cast<const bf16x8*>(sB + (16 * i + r16) * kLdsRow + kq * 64 + q * 16);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   } else if constexpr (IN == FORGE_IN_F32) {
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
-      floatx4 a[4], b[4];
+      floatx4 a[NB], b[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NB; ++i) {
         a[i] = *reinterpret_cast<const floatx4*>(sA + (16 * i + r16) * kLdsRow + kq * 64 + q * 16);
         b[i] = *reinterpret_cast<const floatx4*>(sB + (16 * i + r16) * kLdsRow + kq * 64 + q * 16);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
     }
   } else {  // fp8 e4m3 (OCP), 16x16x128; format 0 = e4m3 for both operands, unit (2^0) block scales
-    intx8 a[4], b[4];
+    intx8 a[NB], b[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const unsigned char* pa = sA + (16 * i + r16) * kLdsRow + q * 32;
       const unsigned char* pb = sB + (16 * i + r16) * kLdsRow + q * 32;
       const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa), a1 = *reinterpret_cast<const u32x4*>(pa + 16);
@@ -176,27 +187,30 @@ __device__ __forceinline__ void mma_slab(floatx4 (&acc)[4][4], const unsigned ch
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
   }
 }
 
-// Accumulate the full gradient of tile (n0, k0) over all T tokens into acc (per wave).
-// Ends with a barrier, so the caller may reuse the LDS.
-template <int IN>
-__device__ __forceinline__ void contract_tile(floatx4 (&acc)[4][4], unsigned char* smem, const GemmArgs& g, int n0,
-                                              int k0) {
+// Accumulate the full gradient of the S x S tile (n0, k0) over all T tokens into acc (per
+// wave).  Ends with a barrier, so the caller may reuse the LDS.
+template <int IN, int S>
+__device__ __forceinline__ void contract_tile(floatx4 (&acc)[SmallTile<S>::NB][SmallTile<S>::NB], unsigned char* smem,
+                                              const GemmArgs& g, int n0, int k0) {
   constexpr int ESZ = InT<IN>::ESZ, TK = InT<IN>::TK, RG = InT<IN>::RG;
+  constexpr int NB = SmallTile<S>::NB, kPanel = SmallTile<S>::PANEL, kStage = SmallTile<S>::STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // loader role: threads 0..127 fetch the dY panel, 128..255 the X panel
+  // loader role: threads 0..127 fetch the dY panel, 128..255 the X panel; a panel is S * ESZ / 16
+  // chunks of 16 bytes times RG groups of 8 tokens (all 128 threads for S = 128, half for S = 64)
   const int op = tid >> 7, lt = tid & 127, rg = lt % RG, ch = lt / RG;
+  const bool loader = lt < (S * ESZ / 16) * RG;
   const unsigned char* src = op ? static_cast<const unsigned char*>(g.X) + (int64_t)k0 * ESZ
                                 : static_cast<const unsigned char*>(g.dY) + (int64_t)n0 * ESZ;
   src += ch * 16;
@@ -204,7 +218,7 @@ __device__ __forceinline__ void contract_tile(floatx4 (&acc)[4][4], unsigned cha
   const int64_t T = g.T;
   const int nsl = (int)((T + TK - 1) / TK);
 
-  // wave tile: rows wm*64.. of the dY panel, rows wn*64.. of the X panel
+  // wave tile: rows wm * S / 2.. of the dY panel, rows wn * S / 2.. of the X panel
   const int wm = wave >> 1, wn = wave & 1;
 
   u32x4 buf[8];
@@ -216,36 +230,48 @@ __device__ __forceinline__ void contract_tile(floatx4 (&acc)[4][4], unsigned cha
     }
   };
 
-  if (nsl > 0) {
+  if (nsl > 0 && loader) {
     load(0);
     store_transposed<IN>(smem + op * kPanel, buf, ch, rg);
   }
   __syncthreads();
   for (int s = 0; s < nsl; ++s) {
     unsigned char* stage = smem + (s & 1) * kStage;
-    if (s + 1 < nsl) load(s + 1);
-    mma_slab<IN>(acc, stage + wm * 64 * kLdsRow, stage + kPanel + wn * 64 * kLdsRow, lane);
-    if (s + 1 < nsl) store_transposed<IN>(smem + ((s + 1) & 1) * kStage + op * kPanel, buf, ch, rg);
+    const bool more = s + 1 < nsl && loader;
+    if (more) load(s + 1);
+    mma_slab<IN, NB>(acc, stage + wm * (S / 2) * kLdsRow, stage + kPanel + wn * (S / 2) * kLdsRow, lane);
+    if (more) store_transposed<IN>(smem + ((s + 1) & 1) * kStage + op * kPanel, buf, ch, rg);
     __syncthreads();
   }
 }
 
-// Stage the accumulators of the 128 x 128 tile in LDS as fp32 [128][kEpiLd], multiplied by
-// `scale`, so that each thread can then read 16 consecutive columns of one row.
-__device__ __forceinline__ void stage_acc(float* st, const floatx4 (&acc)[4][4], float scale) {
+// Stage the accumulators of the S x S tile in LDS as fp32 [S][kEpiLd], multiplied by `scale`,
+// so that each thread can then read 16 consecutive columns of one row.
+template <int S>
+__device__ __forceinline__ void stage_acc(float* st, const floatx4 (&acc)[SmallTile<S>::NB][SmallTile<S>::NB],
+                                          float scale) {
+  constexpr int NB = SmallTile<S>::NB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        st[(wm * 64 + 16 * i + 4 * q + r) * kEpiLd + wn * 64 + 16 * j + r16] = acc[i][j][r] * scale;
+        st[(wm * (S / 2) + 16 * i + 4 * q + r) * kEpiLd + wn * (S / 2) + 16 * j + r16] = acc[i][j][r] * scale;
 }
 
-__device__ __forceinline__ void read_seg16(float (&g)[16], const float* st, int row, int kseg) {
-  const float* p = st + row * kEpiLd + kseg * 16;
+// Row and first column (within the tile) of this thread's segment s of 16 elements.
+template <int S>
+__device__ __forceinline__ void small_seg(int s, int& row, int& col) {
+  const int seg = (int)threadIdx.x + kThreads * s;
+  row = seg / SmallTile<S>::SEGS_PER_ROW;
+  col = (seg % SmallTile<S>::SEGS_PER_ROW) * 16;
+}
+
+__device__ __forceinline__ void read_seg16(float (&g)[16], const float* st, int row, int col) {
+  const float* p = st + row * kEpiLd + col;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * q);

@@ -18,9 +18,9 @@ FusedFn select_fused2(int wide, int w_type, int opt);
 // fp8 inputs, LDS-DMA path: same tiles.
 template <int ST>
 FusedFn select_fused8(int wide, int w_type, int opt);
-// register-staged 128 x 128 path for input format IN.
+// register-staged path for input format IN on tiles of side `tile` (128, or 64 for fp32).
 template <int IN>
-FusedFn select_fused1(int w_type, int s_type, int opt);
+FusedFn select_fused1(int w_type, int s_type, int opt, int tile);
 
 extern template FusedFn select_fused2<FORGE_S_F32>(int, int, int);
 extern template FusedFn select_fused2<FORGE_S_Q8>(int, int, int);
@@ -28,8 +28,8 @@ extern template FusedFn select_fused2<FORGE_S_Q8D>(int, int, int);
 extern template FusedFn select_fused8<FORGE_S_F32>(int, int, int);
 extern template FusedFn select_fused8<FORGE_S_Q8>(int, int, int);
 extern template FusedFn select_fused8<FORGE_S_Q8D>(int, int, int);
-extern template FusedFn select_fused1<FORGE_IN_F32>(int, int, int);
-extern template FusedFn select_fused1<FORGE_IN_BF16>(int, int, int);
-extern template FusedFn select_fused1<FORGE_IN_FP8>(int, int, int);
+extern template FusedFn select_fused1<FORGE_IN_F32>(int, int, int, int);
+extern template FusedFn select_fused1<FORGE_IN_BF16>(int, int, int, int);
+extern template FusedFn select_fused1<FORGE_IN_FP8>(int, int, int, int);
 
 }  // namespace forge

@@ -17,7 +17,7 @@ namespace plan {
 constexpr int kRows = 256;      // full tile rows (n) on the LDS-DMA paths
 constexpr int kCols = 128;      // tile columns (k); a wide tile spans two
 constexpr int kHalfRows = 128;  // half tile rows
-constexpr int kSmallTile = 128; // register-staged path: 128 x 128 tiles
+constexpr int kSmallTile = 128; // register-staged path: 128 x 128 tiles (64 x 64 for small fp32 layers)
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each
 // with its own L2.  Give every XCD a contiguous run of tile ids, and inside a run walk the
@@ -136,7 +136,16 @@ struct Launch {
   int kind;
   GemmArgs g;
   unsigned grid;  // workgroups
+  int tile;       // LAUNCH_SMALL: side of the square tiles (128 or 64)
 };
+
+// Register-staged path: fp32 inputs, whose MFMA rate is a sixteenth of bf16's, are bound by the
+// matrix cores of the CUs that hold a tile; with fewer 128 x 128 tiles than CUs they take
+// 64 x 64 tiles (four times the workgroups, each a quarter of the work).
+inline int small_tile(int in_type, const GemmArgs& g, int cus) {
+  const long tiles = (long)(g.N / kSmallTile) * (long)(g.K / kSmallTile);
+  return in_type == FORGE_IN_F32 && tiles < cus ? 64 : kSmallTile;
+}
 
 // The launches of the fused step (fused = 1) or of the GEMM (fused = 0) for inputs of type
 // in_type on a device with `cus` compute units (two workgroup slots each on the 256 x 128
@@ -159,14 +168,15 @@ inline int plan_launches(int in_type, const GemmArgs& g, int cus, int fused, Lau
         rest.nb_base = wp.nw;
         rest.nbn -= wp.nw;
       }
-      out[n++] = Launch{LAUNCH_WIDE, wide, (unsigned)(wide.nbn * (wide.nbk / 2))};
+      out[n++] = Launch{LAUNCH_WIDE, wide, (unsigned)(wide.nbn * (wide.nbk / 2)), 0};
       if (rest.nbn == 0 || rest.nbk == 0) return n;
     }
     const unsigned grid = kind == LAUNCH_V2 ? plan_split(rest, 2 * cus) : (unsigned)(rest.nbn * rest.nbk);
-    out[n++] = Launch{kind, rest, grid};
+    out[n++] = Launch{kind, rest, grid, 0};
     return n;
   }
-  out[n++] = Launch{LAUNCH_SMALL, g, (unsigned)((g.N / kSmallTile) * (g.K / kSmallTile))};
+  const int t = small_tile(in_type, g, cus);
+  out[n++] = Launch{LAUNCH_SMALL, g, (unsigned)((g.N / t) * (g.K / t)), t};
   return n;
 }
 

@@ -1,6 +1,6 @@
 // plan_check.cpp -- host check of the launch plans and tile mappings in forge_plan.h, the code
 // the kernels and launchers run: for many weight shapes, token counts, CU counts, input types
-// and both the fused step and the GEMM, every 128 x 128 block of W must be covered by exactly
+// and both the fused step and the GEMM, every 64 x 64 block of W must be covered by exactly
 // one workgroup, every tile must lie inside W, and every grid must be non-empty and exact.
 #include <cstdio>
 #include <cstdlib>
@@ -31,11 +31,12 @@ static void check(int in_type, long N, long K, long T, int cus, int fused) {
   Launch L[2];
   const int n = plan_launches(in_type, g, cus, fused, L);
   CHECK(n >= 1 && n <= 2, "N=%ld K=%ld: %d launches", N, K, n);
-  std::vector<int> hit((size_t)(N / 128) * (size_t)(K / 128), 0);
+  std::vector<int> hit((size_t)(N / 64) * (size_t)(K / 64), 0);
+  // coverage is counted on 64 x 64 blocks (the smallest tile)
   auto mark = [&](long n0, long k0, long rows, long cols) -> bool {
-    if (n0 < 0 || k0 < 0 || n0 % 128 || k0 % 128 || n0 + rows > N || k0 + cols > K) return false;
-    for (long r = n0 / 128; r < (n0 + rows) / 128; ++r)
-      for (long c = k0 / 128; c < (k0 + cols) / 128; ++c) ++hit[(size_t)r * (size_t)(K / 128) + (size_t)c];
+    if (n0 < 0 || k0 < 0 || n0 % 64 || k0 % 64 || n0 + rows > N || k0 + cols > K) return false;
+    for (long r = n0 / 64; r < (n0 + rows) / 64; ++r)
+      for (long c = k0 / 64; c < (k0 + cols) / 64; ++c) ++hit[(size_t)r * (size_t)(K / 64) + (size_t)c];
     return true;
   };
   for (int i = 0; i < n; ++i) {
@@ -60,10 +61,13 @@ static void check(int in_type, long N, long K, long T, int cus, int fused) {
           rows = kRows, cols = kCols;
           break;
         default: {
-          const int nbN = (int)(N / kSmallTile), nbK = (int)(K / kSmallTile);
+          const int t = L[i].tile;
+          CHECK(t == 128 || (t == 64 && in_type == FORGE_IN_F32), "bad small tile %d", t);
+          const int nbN = (int)(N / t), nbK = (int)(K / t);
+          CHECK(L[i].grid == (unsigned)(nbN * nbK), "bad small grid");
           int nb, kb;
           tile_coords_at((int)b, nbN, nbK, nb, kb);
-          n0 = nb * kSmallTile, k0 = kb * kSmallTile, rows = kSmallTile, cols = kSmallTile;
+          n0 = nb * t, k0 = kb * t, rows = t, cols = t;
         }
       }
       CHECK(mark(n0, k0, rows, cols), "N=%ld K=%ld T=%ld cus=%d launch %d kind %d wg %u: tile (%d, %d) outside W", N,
@@ -72,7 +76,7 @@ static void check(int in_type, long N, long K, long T, int cus, int fused) {
   }
   for (size_t j = 0; j < hit.size(); ++j)
     CHECK(hit[j] == 1, "N=%ld K=%ld T=%ld cus=%d in=%d fused=%d: block (%zu, %zu) covered %d times", N, K, T, cus,
-          in_type, fused, j / (size_t)(K / 128), j % (size_t)(K / 128), hit[j]);
+          in_type, fused, j / (size_t)(K / 64), j % (size_t)(K / 64), hit[j]);
 }
 
 int main() {

@@ -184,6 +184,42 @@ def test_wgrad_gemm_matches_oracle(lib, in_fmt):
     print(f"  max |err| / bound = {float(np.max(err / np.maximum(tau, 1e-300))):.3e}")
 
 
+# fp32 inputs take 64 x 64 tiles while a weight has fewer 128 x 128 tiles than the device has
+# CUs (256 x 384 above), and 128 x 128 tiles from there on (2048 x 2048: 256 tiles).
+F32_128 = [("adamw", "f32"), ("lion", "int8"), ("nadam", "int8dyn"), ("sgd_momentum", "f32")]
+
+
+@pytest.mark.parametrize("opt,state_fmt", F32_128, ids=["-".join(c) for c in F32_128])
+def test_f32_large_tiles_exact_oracle_fed(lib, opt, state_fmt):
+    Nn = Kn = 2048
+    rng = np.random.default_rng(91)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(92, Nn, Kn, "f32")
+    m, v = _init_states(opt, state_fmt, rng, Nn, Kn)
+    for i, t in enumerate((1, 3)):
+        _say("f32 128x128 tiles exact oracle-fed", opt, state_fmt, Nn, Kn, "step", t)
+        X, dY = synth.integer_case(390 + i, T, Nn, Kn, "f32")
+        ref = wgrad.step(X, dY, W, m, v, opt, h, t, 23, "f32", state_fmt)
+        d = P.DeviceStep(W, m, v, "f32", state_fmt)
+        pre = d.fused(lib, X, dY, opt, h, t, 23, preround=True)
+        gW, gm, gv = d.host()
+        _compare(ref, gW, gm, gv, pre.cpu().numpy(), "f32", state_fmt, W, tag=f"step {t}",
+                 lion=(h, t, m, v) if opt == "lion" else None)
+        W, m, v = ref["W"], ref["m"], ref["v"]
+
+
+def test_f32_large_tiles_wgrad_gemm_exact(lib):
+    Nn = Kn = 2048
+    _say("wgrad gemm f32 128x128 tiles", Nn, Kn)
+    X, dY = synth.integer_case(395, T, Nn, Kn, "f32")
+    dW = torch.empty((Nn, Kn), dtype=torch.float32, device="cuda")
+    Xd, xs = P.dev_operand(X)
+    Dd, ds = P.dev_operand(dY)
+    lib.wgrad_gemm(Xd, Dd, dW, x_scale=xs, dy_scale=ds)
+    ref = wgrad.wgrad(wgrad.decode_operand(X), wgrad.decode_operand(dY))
+    np.testing.assert_array_equal(dW.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("Tn,Nn,Kn", [(200, 256, 384), (128, 384, 256), (1, 128, 128), (333, 640, 128)])
 def test_dgrad_matches_oracle(lib, Tn, Nn, Kn):
     _say("dgrad", Tn, Nn, Kn)
