@@ -342,6 +342,28 @@ def _llama_block(forge, reps, randn):
         if r >= 2:
             ub.append(ev[0].elapsed_time(ev[-1]))
     del dW
+    # the same block with each layer's dgrad and step in one launch (forge_linear_backward_step_fused);
+    # one workspace of counters serves the layers one after another on the stream
+    ws = torch.empty(max(forge.backward_workspace_bytes(d["K"]) for d in layers) // 4, dtype=torch.int32,
+                     device="cuda")
+    ob = []
+    ol = [[] for _ in layers]
+    for r in range(reps + 2):
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i, d in enumerate(layers):
+            forge.linear_backward_step_fused(d["X"], d["dY"], d["W"], d["dX"], d["m"], d["v"], opt="adamw",
+                                             hyper=w.hyper, step=2 * reps + 5 + r, seed=synth.sr_seed(3, i),
+                                             workspace=ws)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ob.append(ev[0].elapsed_time(ev[-1]))
+            for i in range(len(layers)):
+                ol[i].append(ev[i].elapsed_time(ev[i + 1]))
+    if int(ws[1].item()) != 0:
+        raise RuntimeError("the one-launch backward step reported a schedule fault")
+    del ws
     # the gradient floor of a framework-style unfused step: every layer's dW is produced by the
     # backward pass and alive until the optimizer runs over all of them (measured as the peak
     # memory above what the fused block holds)
@@ -363,7 +385,9 @@ def _llama_block(forge, reps, randn):
         "block_us": pctl(block), "tflops_wgrad_plus_dgrad": round(flop / (b50 * 1e-6) / 1e12, 1),
         "per_layer_us_p50": {d["name"]: pctl(per_layer[i])["p50"] for i, d in enumerate(layers)},
         "unfused_block_us": pctl(ub), "unfused_all_gradients_peak_extra_bytes": int(all_grads_extra),
-        "fused_peak_extra_bytes": int(fused_extra)}
+        "fused_peak_extra_bytes": int(fused_extra),
+        "one_launch_block_us": pctl(ob),
+        "one_launch_per_layer_us_p50": {d["name"]: pctl(ol[i])["p50"] for i, d in enumerate(layers)}}
     del layers
     return out
 

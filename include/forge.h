@@ -182,6 +182,38 @@ forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tenso
                                         void* stream);
 
 /*
+ * forge_linear_backward_step_fused -- what forge_linear_backward_step computes (dX from the
+ * weight as it was before the step, then the fused step of W, m, v), in one kernel launch
+ * after a one-workgroup clear of the workspace.  FORGE explainer (gist.science), Technical
+ * Summary section 5, limitations (the input gradient is read before the weight update), and
+ * section 2 "Core Mechanism" (the step).  In the launch, workgroups take the dX tiles (256
+ * tokens x 128 columns) and the step's tiles of W from work queues, every dX tile before any step
+ * tile; a step tile contracts dY and X, then, before it writes W, waits until every dX tile of
+ * its 128 columns has finished reading them.  dX, W, m and v come out bitwise as
+ * forge_linear_backward_step leaves them.
+ *
+ * Arguments as forge_linear_backward_step (BF16 X, dY, W and dX), and N % 256 == 0, K % 128 == 0
+ * (else FORGE_ERR_SHAPE).  workspace: device memory of at least
+ * forge_backward_workspace_bytes(K) bytes, 4-byte aligned, owned by the caller and overlapping
+ * no tensor of the call (FORGE_ERR_ARG / FORGE_ERR_LAYOUT / FORGE_ERR_ALIAS); its contents
+ * before the call do not matter, and the call overwrites them.  Two calls that share a
+ * workspace must not run at the same time (on different streams, say).  Once the stream has
+ * passed the call, the int32 at byte offset 4 of the workspace is 0.  It is nonzero only on a
+ * fault of the schedule: bit 0 if a step tile's wait reached its bound (seconds), bit 1 if a
+ * workgroup found no work left (calls sharing the workspace overlapped); the tiles concerned
+ * were then not updated.
+ */
+forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge_tensor* dY,
+                                              forge_tensor* W, forge_tensor* dX, forge_tensor* m,
+                                              forge_tensor* v, const forge_hyper* hyper, int32_t opt,
+                                              int64_t step, uint64_t seed,
+                                              const forge_step_opts* opts, void* workspace,
+                                              int64_t workspace_bytes, void* stream);
+/* Bytes of workspace forge_linear_backward_step_fused needs for a weight of K columns
+ * (4 x (26 + K / 128)); -1 for K < 0 or K > 2^40. */
+int64_t forge_backward_workspace_bytes(int64_t K);
+
+/*
  * Unfused two-phase baseline (Technical Summary section 1 "The Problem"): the gradient is
  * materialised in a caller-owned fp32 buffer dW[N, K] and a separate kernel applies the rule.
  * The contraction and the rule are the same device code as the fused path, so for the same

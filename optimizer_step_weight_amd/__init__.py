@@ -65,6 +65,9 @@ def _lib():
         L.forge_wgrad_step.argtypes = [T, T, T, T, T, H, i32, i64, u64, O, vp]
         L.forge_dgrad.argtypes = [T, T, T, vp]
         L.forge_linear_backward_step.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp]
+        L.forge_linear_backward_step_fused.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp, i64, vp]
+        L.forge_backward_workspace_bytes.argtypes = [i64]
+        L.forge_backward_workspace_bytes.restype = i64
         L.forge_wgrad_gemm.argtypes = [T, T, T, vp]
         L.forge_optimizer_step.argtypes = [T, T, T, T, H, i32, i64, u64, O, vp]
         L.forge_step_scalars.argtypes = [i32, H, i64, _P(ctypes.c_float), i32]
@@ -77,8 +80,8 @@ def _lib():
         L.forge_clock_sample.restype = st
         L.forge_realtime_hz.restype = ctypes.c_double
         L.forge_device_check.argtypes = [i32]
-        for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_wgrad_gemm",
-                  "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
+        for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_linear_backward_step_fused",
+                  "forge_wgrad_gemm", "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
             getattr(L, f).restype = st
         from . import _build
         built, want = L.forge_build_id().decode(), _build.source_hash()
@@ -214,6 +217,31 @@ def linear_backward_step(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=Non
         _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, dyn)),
         _ref(_tensor(v, v_scale, dyn)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
+
+
+def backward_workspace_bytes(K: int) -> int:
+    """Workspace bytes linear_backward_step_fused needs for a weight of K columns."""
+    return int(_lib().forge_backward_workspace_bytes(int(K)))
+
+
+def linear_backward_step_fused(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=None, step: int, seed: int,
+                               m_scale=None, v_scale=None, w_preround_out=None, sr=True, state_map="linear",
+                               workspace=None, stream=None):
+    """dgrad and the fused step in one launch (forge_linear_backward_step_fused).  `workspace` is a
+    device tensor of at least backward_workspace_bytes(K) bytes; one is allocated when it is None.
+    Returns the workspace (its int32 word 1 is nonzero if a wait hit its bound)."""
+    import torch
+    o = _opts(w_preround_out, sr, W)
+    dyn = _dyn(state_map)
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_bytes(W.shape[1]) // 4, dtype=torch.int32, device=W.device)
+    _on_device(workspace, "workspace")
+    _check(_lib().forge_linear_backward_step_fused(
+        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, dyn)),
+        _ref(_tensor(v, v_scale, dyn)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return workspace
 
 
 def wgrad_gemm(X, dY, dW, *, x_scale=None, dy_scale=None, stream=None):

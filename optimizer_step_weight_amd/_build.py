@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-con
 # translation unit, so the sources compile in parallel.
 SOURCES = ["forge_fused2_q8.hip", "forge_fused2_q8d.hip", "forge_fused1_f32.hip", "forge_fused1_bf16.hip",
            "forge_fused1_fp8.hip", "forge_fused8_q8.hip", "forge_fused8_q8d.hip", "forge_fused2_f32.hip",
-           "forge_fused8_f32.hip", "forge_kernels.hip", "forge_measure.hip", "forge_host.cpp"]
+           "forge_fused8_f32.hip", "forge_backward.hip", "forge_kernels.hip", "forge_measure.hip", "forge_host.cpp"]
 
 
 def source_hash(root: str = ROOT) -> str:

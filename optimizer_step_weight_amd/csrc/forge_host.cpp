@@ -412,24 +412,22 @@ forge_status forge_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_te
   return to_status(forge::launch_dgrad(dY->data, W->data, dX->data, T, N, K, stream));
 }
 
-forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
-                                        forge_tensor* dX, forge_tensor* m, forge_tensor* v, const forge_hyper* hyper,
-                                        int32_t opt, int64_t step, uint64_t seed, const forge_step_opts* opts,
-                                        void* stream) {
-  g_last_error.clear();
-  // Validate both calls before enqueueing either, so that an error leaves every buffer untouched.
+// Validation shared by the two backward-step entry points: both calls' arguments, before either
+// is enqueued, so that an error leaves every buffer untouched.
+static forge_status validate_backward(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* dX,
+                                      forge_tensor* m, forge_tensor* v, const forge_hyper* hyper, int32_t opt,
+                                      int64_t step, uint64_t seed, const forge_step_opts* opts, forge::GemmArgs* g,
+                                      StepPlan* plan, Range* ranges, int* n_ranges) {
   Range ins[4], outs[6];
   int n_in = 0, n_out = 0, in_type = 0;
-  forge::GemmArgs g{};
   forge_status st;
-  if ((st = validate_inputs(X, dY, &in_type, &g, ins, &n_in)) != FORGE_OK) return st;
-  StepPlan plan;
-  if ((st = validate_step_outputs(g.N, g.K, W, m, v, hyper, opt, step, seed, opts, &plan, outs, &n_out)) != FORGE_OK)
+  if ((st = validate_inputs(X, dY, &in_type, g, ins, &n_in)) != FORGE_OK) return st;
+  if ((st = validate_step_outputs(g->N, g->K, W, m, v, hyper, opt, step, seed, opts, plan, outs, &n_out)) != FORGE_OK)
     return st;
   if ((st = check_tensor(dX, "dX")) != FORGE_OK) return st;
   if (in_type != forge::FORGE_IN_BF16 || W->dtype != FORGE_BF16 || dX->dtype != FORGE_BF16)
     return fail(FORGE_ERR_DTYPE, "the backward step takes BF16 X, dY, W and dX");
-  if (dX->rows != g.T || dX->cols != g.K) return fail(FORGE_ERR_SHAPE, "dX must be [T, K]");
+  if (dX->rows != g->T || dX->cols != g->K) return fail(FORGE_ERR_SHAPE, "dX must be [T, K]");
   const Range rdx = range_of(dX->data, bytes_of(dX), "dX");
   for (int i = 0; i < n_out; ++i) {
     if (overlap(outs[i], rdx)) return fail(FORGE_ERR_ALIAS, "%s overlaps dX", outs[i].name);
@@ -438,8 +436,68 @@ forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tenso
   }
   for (int j = 0; j < n_in; ++j)
     if (overlap(rdx, ins[j])) return fail(FORGE_ERR_ALIAS, "dX overlaps %s", ins[j].name);
+  int n = 0;
+  for (int j = 0; j < n_in; ++j) ranges[n++] = ins[j];
+  for (int i = 0; i < n_out; ++i) ranges[n++] = outs[i];
+  ranges[n++] = rdx;
+  *n_ranges = n;
+  return FORGE_OK;
+}
+
+forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                        forge_tensor* dX, forge_tensor* m, forge_tensor* v, const forge_hyper* hyper,
+                                        int32_t opt, int64_t step, uint64_t seed, const forge_step_opts* opts,
+                                        void* stream) {
+  g_last_error.clear();
+  forge::GemmArgs g{};
+  StepPlan plan;
+  Range ranges[11];
+  int n_ranges = 0;
+  forge_status st;
+  if ((st = validate_backward(X, dY, W, dX, m, v, hyper, opt, step, seed, opts, &g, &plan, ranges, &n_ranges)) !=
+      FORGE_OK)
+    return st;
   if ((st = forge_dgrad(dY, W, dX, stream)) != FORGE_OK) return st;
   return forge_wgrad_step(X, dY, W, m, v, hyper, opt, step, seed, opts, stream);
+}
+
+int64_t forge_backward_workspace_bytes(int64_t K) {
+  if (K < 0 || K > (int64_t(1) << 40)) return -1;
+  return 4 * forge::backward_workspace_words(K);
+}
+
+forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                              forge_tensor* dX, forge_tensor* m, forge_tensor* v,
+                                              const forge_hyper* hyper, int32_t opt, int64_t step, uint64_t seed,
+                                              const forge_step_opts* opts, void* workspace, int64_t workspace_bytes,
+                                              void* stream) {
+  g_last_error.clear();
+  forge::GemmArgs g{};
+  StepPlan plan;
+  Range ranges[11];
+  int n_ranges = 0;
+  forge_status st;
+  if ((st = validate_backward(X, dY, W, dX, m, v, hyper, opt, step, seed, opts, &g, &plan, ranges, &n_ranges)) !=
+      FORGE_OK)
+    return st;
+  if (g.N % 256 || g.K % 128) return fail(FORGE_ERR_SHAPE, "the one-launch backward step needs N %% 256 == 0 and K %% 128 == 0");
+  // the dX tiles address dY (padded to whole 256-token tiles) and W with 32-bit byte offsets
+  if ((g.T + 256) * g.N * 2 >= (int64_t(1) << 32) || g.N * g.K * 2 >= (int64_t(1) << 32))
+    return fail(FORGE_ERR_SHAPE, "dY (plus one tile of tokens) and W must each stay below 4 GiB");
+  if (g.N * g.K >= (int64_t(1) << 32)) return fail(FORGE_ERR_SHAPE, "N * K must be below 2^32");
+  const int64_t need = forge_backward_workspace_bytes(g.K);
+  if (!workspace) return fail(FORGE_ERR_ARG, "workspace is NULL");
+  if (!aligned4(workspace)) return fail(FORGE_ERR_LAYOUT, "workspace is not 4-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FORGE_ERR_ARG, "workspace has %lld bytes, the call needs %lld", (long long)workspace_bytes,
+                (long long)need);
+  const Range rw = range_of(workspace, need, "workspace");
+  for (int i = 0; i < n_ranges; ++i)
+    if (overlap(rw, ranges[i])) return fail(FORGE_ERR_ALIAS, "workspace overlaps %s", ranges[i].name);
+  if (g.N == 0 || g.K == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  return to_status(forge::launch_backward_step(plan.s_type, opt, g, plan.e, W->data, dX->data,
+                                               static_cast<int*>(workspace), stream));
 }
 
 forge_status forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, float* out, int32_t n_out) {

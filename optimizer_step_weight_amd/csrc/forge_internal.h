@@ -70,4 +70,22 @@ int launch_optimizer(int w_type, int s_type, int opt, const float* dW, int64_t n
                      void* stream);
 int launch_dgrad(const void* dY, const void* W, void* dX, int64_t T, int64_t N, int64_t K, void* stream);
 
+// The backward step in one launch (forge_backward.hip): dX tiles and the fused step's tiles
+// taken from work queues, the step's update of a column block after that block's dX tiles.
+struct BackwardArgs {
+  const uint16_t* W_old;  // W [N, K] bf16 as the dX tiles read it (the weight the step updates)
+  uint16_t* dX;           // [T, K] bf16
+  int* ctr;               // workspace words (forge_backward.hip)
+  int nbT;                // 256-token blocks of dX
+  int n_dgrad;            // dX tiles: nbT x (K / 128)
+  int spin_limit;         // polls of a wait before it gives up
+};
+constexpr int kBackwardSpinLimit = 1 << 21;
+// Workspace words for a weight of K columns.
+int64_t backward_workspace_words(int64_t K);
+int launch_backward_step(int s_type, int opt, const GemmArgs& g, const EpiArgs& e, const void* W_old, void* dX,
+                         int* ctr, void* stream);
+// Workgroup slots of the current device: two per CU.
+int slots_on_current_device();
+
 }  // namespace forge

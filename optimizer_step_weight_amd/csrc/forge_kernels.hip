@@ -101,7 +101,7 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void wgrad_gemm_kernel8(GemmAr
 }
 
 // Workgroup slots on the current device: two 256 x 128 workgroups per CU.
-static int slots_on_current_device() {
+int slots_on_current_device() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;

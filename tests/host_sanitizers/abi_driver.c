@@ -95,6 +95,27 @@ int main(void) {
   EXPECT(forge_optimizer_step(&dW, &W, &m, &v, &h, FORGE_ADAMW, 1, 7, NULL, NULL), VALID);
   EXPECT(forge_dgrad(&dY, &W, &dX, NULL), VALID);
   EXPECT(forge_linear_backward_step(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, NULL), VALID);
+  {
+    void* ws = dev(7);
+    const int64_t need = forge_backward_workspace_bytes(K);
+    EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, ws, need, NULL),
+           VALID);
+    EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, ws, need - 1,
+                                            NULL),
+           FORGE_ERR_ARG);
+    EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, NULL, need, NULL),
+           FORGE_ERR_ARG);
+    EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, W.data, need,
+                                            NULL),
+           FORGE_ERR_ALIAS);
+    EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, ws, INT64_MIN,
+                                            NULL),
+           FORGE_ERR_ARG);
+    if (forge_backward_workspace_bytes(-5) != -1 || forge_backward_workspace_bytes(INT64_MAX) != -1) {
+      fprintf(stderr, "workspace size of a bad K\n");
+      return 1;
+    }
+  }
 
   /* ---- NULL arguments */
   EXPECT(forge_wgrad_step(NULL, &dY, &W, &m, &v, &h, FORGE_ADAMW, 1, 7, NULL, NULL), FORGE_ERR_ARG);

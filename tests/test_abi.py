@@ -125,6 +125,46 @@ def test_dgrad_and_unfused_validation(forge):
     assert L.forge_optimizer_step(r(dW), r(_t(f, 256, 384, f.BF16, 4 * GB)), None, None, r(h), 6, 1, 0, None, None) == 5
 
 
+def test_one_launch_backward_validation(forge):
+    """forge_linear_backward_step_fused: the backward step's checks, its own shape rule
+    (N % 256, K % 128) and the workspace's size, alignment and aliasing."""
+    f = forge
+    GB = 1 << 30
+    r = ctypes.byref
+    L = f._lib()
+    T, N, K = 100, 256, 384
+    assert f.backward_workspace_bytes(K) == 4 * (26 + K // 128)
+    assert f.backward_workspace_bytes(-1) == -1
+    h = f._hyper(synth.default_hyper("adamw"))
+    need = f.backward_workspace_bytes(K)
+
+    def call(X=None, dY=None, W=None, dX=None, m=None, v=None, ws=FAKE + 9 * GB, nbytes=need):
+        X = X or _t(f, T, K, f.BF16)
+        dY = dY or _t(f, T, N, f.BF16, GB)
+        W = W or _t(f, N, K, f.BF16, 2 * GB)
+        dX = dX or _t(f, T, K, f.BF16, 3 * GB)
+        m = m or _t(f, W.rows, W.cols, f.F32, 4 * GB)
+        v = v or _t(f, W.rows, W.cols, f.F32, 5 * GB)
+        return L.forge_linear_backward_step_fused(r(X), r(dY), r(W), r(dX), r(m), r(v), r(h), 0, 1, 1, None, ws,
+                                                  nbytes, None)
+
+    assert call(ws=None) == 1                                             # no workspace
+    assert call(nbytes=need - 4) == 1                                     # workspace too small
+    assert call(ws=FAKE + 9 * GB + 2) == 4                                # workspace misaligned
+    assert call(ws=FAKE + 2 * GB + 64) == 5                               # workspace inside W
+    assert call(ws=FAKE + 3 * GB) == 5                                    # workspace is dX
+    assert call(dX=_t(f, T, K, f.F32, 3 * GB)) == 3                       # dX must be bf16
+    assert call(dX=_t(f, T, K, f.BF16, 2 * GB)) == 5                      # dX overlaps W
+    dY128 = _t(f, T, 128, f.BF16, GB)                                     # N = 128: not a multiple of 256
+    assert call(dY=dY128, W=_t(f, 128, K, f.BF16, 2 * GB)) == 2
+    assert "256" in f.last_error()
+    # the same arguments are accepted by the two-launch entry point's checks up to the device
+    X, dY, W, dX = _t(f, T, K, f.BF16), dY128, _t(f, 128, K, f.BF16, 2 * GB), _t(f, T, K, f.BF16, 3 * GB)
+    m, v = _t(f, 128, K, f.F32, 4 * GB), _t(f, 128, K, f.F32, 5 * GB)
+    assert L.forge_linear_backward_step(r(X), r(dY), r(W), r(dX), r(m), r(_t(f, 128, 200, f.F32, 5 * GB)), r(h), 0,
+                                        1, 1, None, None) == 2
+
+
 @pytest.mark.parametrize("opt", synth.OPTIMIZERS)
 @pytest.mark.parametrize("t", [1, 2, 5, 6, 50])
 def test_host_scalars_match_oracle(forge, opt, t):
