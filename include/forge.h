@@ -29,7 +29,9 @@
  *     device, aligned to 16 bytes.  All buffers are owned by the caller; the
  *     library keeps no pointer to them after a call returns.  Its only global
  *     state is a per-device cache (whether the device passed the gfx950 check,
- *     and its compute-unit count), written once per device and never cleared.
+ *     its compute-unit count, the address of the counter array of
+ *     forge_linear_backward_step_fused_noalloc), written once per device and
+ *     never cleared, and that counter array itself (a static device array).
  *   - Shapes: X[T, K] layer input, dY[T, N] upstream gradient, W[N, K] weight
  *     (PyTorch nn.Linear layout), dW[N, K], dX[T, K].  N and K must be
  *     multiples of 128; T may be any value >= 0 (a ragged final token slab is
@@ -209,6 +211,25 @@ forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge
                                               int64_t step, uint64_t seed,
                                               const forge_step_opts* opts, void* workspace,
                                               int64_t workspace_bytes, void* stream);
+/*
+ * forge_linear_backward_step_fused_noalloc -- for callers that cannot allocate device memory
+ * or hand over a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): forge_linear_backward_step_fused with the counters in a static device
+ * array of the library (16 KiB, one per device, held until the process ends; its address is
+ * resolved on the first call on each device).  Allocates nothing.  Same arguments and results
+ * as forge_linear_backward_step_fused without the workspace; K must not exceed 520960
+ * ((4096 - 26) x 128 columns, else FORGE_ERR_SHAPE).  Every call on a device uses that device's
+ * one array: calls on one device that overlap in time (on different streams, say) race and
+ * must not be made; calls in order on one stream are fine, each clears the counters first.
+ * The error word of forge_linear_backward_step_fused is kept in that array and is not
+ * reported.
+ */
+forge_status forge_linear_backward_step_fused_noalloc(const forge_tensor* X, const forge_tensor* dY,
+                                                      forge_tensor* W, forge_tensor* dX,
+                                                      forge_tensor* m, forge_tensor* v,
+                                                      const forge_hyper* hyper, int32_t opt,
+                                                      int64_t step, uint64_t seed,
+                                                      const forge_step_opts* opts, void* stream);
 /* Bytes of workspace forge_linear_backward_step_fused needs for a weight of K columns
  * (4 x (26 + K / 128)); -1 for K < 0 or K > 2^40. */
 int64_t forge_backward_workspace_bytes(int64_t K);

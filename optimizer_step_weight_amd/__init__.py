@@ -66,6 +66,7 @@ def _lib():
         L.forge_dgrad.argtypes = [T, T, T, vp]
         L.forge_linear_backward_step.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp]
         L.forge_linear_backward_step_fused.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp, i64, vp]
+        L.forge_linear_backward_step_fused_noalloc.argtypes = [T, T, T, T, T, T, H, i32, i64, u64, O, vp]
         L.forge_backward_workspace_bytes.argtypes = [i64]
         L.forge_backward_workspace_bytes.restype = i64
         L.forge_wgrad_gemm.argtypes = [T, T, T, vp]
@@ -81,7 +82,8 @@ def _lib():
         L.forge_realtime_hz.restype = ctypes.c_double
         L.forge_device_check.argtypes = [i32]
         for f in ("forge_wgrad_step", "forge_dgrad", "forge_linear_backward_step", "forge_linear_backward_step_fused",
-                  "forge_wgrad_gemm", "forge_optimizer_step", "forge_step_scalars", "forge_device_check"):
+                  "forge_linear_backward_step_fused_noalloc", "forge_wgrad_gemm", "forge_optimizer_step",
+                  "forge_step_scalars", "forge_device_check"):
             getattr(L, f).restype = st
         from . import _build
         built, want = L.forge_build_id().decode(), _build.source_hash()
@@ -242,6 +244,19 @@ def linear_backward_step_fused(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyp
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return workspace
+
+
+def linear_backward_step_fused_noalloc(X, dY, W, dX, m=None, v=None, *, opt="adamw", hyper=None, step: int,
+                                       seed: int, m_scale=None, v_scale=None, w_preround_out=None, sr=True,
+                                       state_map="linear", stream=None):
+    """linear_backward_step_fused with the library's own counters: allocates nothing
+    (forge_linear_backward_step_fused_noalloc).  Calls on one device must not overlap."""
+    o = _opts(w_preround_out, sr, W)
+    dyn = _dyn(state_map)
+    _check(_lib().forge_linear_backward_step_fused_noalloc(
+        _ref(_tensor(X)), _ref(_tensor(dY)), _ref(_tensor(W)), _ref(_tensor(dX)), _ref(_tensor(m, m_scale, dyn)),
+        _ref(_tensor(v, v_scale, dyn)), ctypes.byref(_hyper(hyper)), _opt(opt), int(step),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ref(o), _stream(stream)))
 
 
 def wgrad_gemm(X, dY, dW, *, x_scale=None, dy_scale=None, stream=None):

@@ -20,8 +20,16 @@
 // no wave is left waiting.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "forge_dgrad.h"
 #include "forge_fused2.h"
+
+// The counters of the allocation-free entry point: one array per device, for the life of the
+// process (kBackwardScratchWords words).  Host code never passes this name to a kernel: it is
+// a host-side stand-in; backward_scratch() resolves the device address.
+static __device__ __align__(256) int scratch[forge::kBackwardScratchWords];
 
 namespace forge {
 
@@ -140,6 +148,32 @@ static BackwardFn backward_for(int opt) {
 }
 
 int64_t backward_workspace_words(int64_t K) { return BWD_DONE + K / ml2::BN; }
+
+namespace {
+std::mutex g_scratch_mu;
+std::atomic<int*> g_scratch[64];
+}  // namespace
+
+int backward_scratch(int** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return (int)err;
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  int* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));  // with device `dev` current
+      if (err != hipSuccess) return (int)err;
+      p = static_cast<int*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return (int)hipSuccess;
+}
 
 int launch_backward_step(int s_type, int opt, const GemmArgs& g_in, const EpiArgs& e, const void* W_old, void* dX,
                          int* ctr, void* stream) {

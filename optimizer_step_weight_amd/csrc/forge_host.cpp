@@ -466,6 +466,17 @@ int64_t forge_backward_workspace_bytes(int64_t K) {
   return 4 * forge::backward_workspace_words(K);
 }
 
+// Checks of the one-launch backward step beyond the backward step's own.
+static forge_status validate_one_launch(const forge::GemmArgs& g) {
+  if (g.N % 256 || g.K % 128)
+    return fail(FORGE_ERR_SHAPE, "the one-launch backward step needs N %% 256 == 0 and K %% 128 == 0");
+  // the dX tiles address dY (padded to whole 256-token tiles) and W with 32-bit byte offsets
+  if ((g.T + 256) * g.N * 2 >= (int64_t(1) << 32) || g.N * g.K * 2 >= (int64_t(1) << 32))
+    return fail(FORGE_ERR_SHAPE, "dY (plus one tile of tokens) and W must each stay below 4 GiB");
+  if (g.N * g.K >= (int64_t(1) << 32)) return fail(FORGE_ERR_SHAPE, "N * K must be below 2^32");
+  return FORGE_OK;
+}
+
 forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
                                               forge_tensor* dX, forge_tensor* m, forge_tensor* v,
                                               const forge_hyper* hyper, int32_t opt, int64_t step, uint64_t seed,
@@ -480,11 +491,7 @@ forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge
   if ((st = validate_backward(X, dY, W, dX, m, v, hyper, opt, step, seed, opts, &g, &plan, ranges, &n_ranges)) !=
       FORGE_OK)
     return st;
-  if (g.N % 256 || g.K % 128) return fail(FORGE_ERR_SHAPE, "the one-launch backward step needs N %% 256 == 0 and K %% 128 == 0");
-  // the dX tiles address dY (padded to whole 256-token tiles) and W with 32-bit byte offsets
-  if ((g.T + 256) * g.N * 2 >= (int64_t(1) << 32) || g.N * g.K * 2 >= (int64_t(1) << 32))
-    return fail(FORGE_ERR_SHAPE, "dY (plus one tile of tokens) and W must each stay below 4 GiB");
-  if (g.N * g.K >= (int64_t(1) << 32)) return fail(FORGE_ERR_SHAPE, "N * K must be below 2^32");
+  if ((st = validate_one_launch(g)) != FORGE_OK) return st;
   const int64_t need = forge_backward_workspace_bytes(g.K);
   if (!workspace) return fail(FORGE_ERR_ARG, "workspace is NULL");
   if (!aligned4(workspace)) return fail(FORGE_ERR_LAYOUT, "workspace is not 4-byte aligned");
@@ -498,6 +505,32 @@ forge_status forge_linear_backward_step_fused(const forge_tensor* X, const forge
   if ((st = device_ok()) != FORGE_OK) return st;
   return to_status(forge::launch_backward_step(plan.s_type, opt, g, plan.e, W->data, dX->data,
                                                static_cast<int*>(workspace), stream));
+}
+
+forge_status forge_linear_backward_step_fused_noalloc(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                                      forge_tensor* dX, forge_tensor* m, forge_tensor* v,
+                                                      const forge_hyper* hyper, int32_t opt, int64_t step,
+                                                      uint64_t seed, const forge_step_opts* opts, void* stream) {
+  g_last_error.clear();
+  forge::GemmArgs g{};
+  StepPlan plan;
+  Range ranges[11];
+  int n_ranges = 0;
+  forge_status st;
+  if ((st = validate_backward(X, dY, W, dX, m, v, hyper, opt, step, seed, opts, &g, &plan, ranges, &n_ranges)) !=
+      FORGE_OK)
+    return st;
+  if ((st = validate_one_launch(g)) != FORGE_OK) return st;
+  if (forge::backward_workspace_words(g.K) > forge::kBackwardScratchWords)
+    return fail(FORGE_ERR_SHAPE, "K = %lld is beyond the allocation-free variant's limit of %lld columns",
+                (long long)g.K, (long long)(forge::kBackwardScratchWords - forge::backward_workspace_words(0)) * 128);
+  if (g.N == 0 || g.K == 0) return FORGE_OK;
+  if ((st = device_ok()) != FORGE_OK) return st;
+  int* counters = nullptr;
+  const int herr = forge::backward_scratch(&counters);
+  if (herr != (int)hipSuccess)
+    return fail(FORGE_ERR_LAUNCH, "the device address of the library's counters: %s", hipGetErrorString((hipError_t)herr));
+  return to_status(forge::launch_backward_step(plan.s_type, opt, g, plan.e, W->data, dX->data, counters, stream));
 }
 
 forge_status forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, float* out, int32_t n_out) {

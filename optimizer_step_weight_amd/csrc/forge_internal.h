@@ -83,6 +83,10 @@ struct BackwardArgs {
 constexpr int kBackwardSpinLimit = 1 << 21;
 // Workspace words for a weight of K columns.
 int64_t backward_workspace_words(int64_t K);
+// The allocation-free variant's counters: a static device array of this many words per device;
+// backward_scratch() gives its address on the current device (resolved once per device).
+constexpr int kBackwardScratchWords = 4096;
+int backward_scratch(int** out);
 int launch_backward_step(int s_type, int opt, const GemmArgs& g, const EpiArgs& e, const void* W_old, void* dX,
                          int* ctr, void* stream);
 // Workgroup slots of the current device: two per CU.

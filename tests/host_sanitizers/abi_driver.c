@@ -111,6 +111,7 @@ int main(void) {
     EXPECT(forge_linear_backward_step_fused(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, ws, INT64_MIN,
                                             NULL),
            FORGE_ERR_ARG);
+    EXPECT(forge_linear_backward_step_fused_noalloc(&X, &dY, &W, &dX, &m, &v, &h, FORGE_ADAMW, 3, 7, NULL, NULL), VALID);
     if (forge_backward_workspace_bytes(-5) != -1 || forge_backward_workspace_bytes(INT64_MAX) != -1) {
       fprintf(stderr, "workspace size of a bad K\n");
       return 1;

@@ -24,6 +24,10 @@ int launch_backward_step(int, int, const GemmArgs&, const EpiArgs&, const void*,
   return refuse();
 }
 int64_t backward_workspace_words(int64_t K) { return 26 + K / 128; }
+int backward_scratch(int** out) {
+  *out = nullptr;
+  return refuse();
+}
 }  // namespace forge
 
 extern "C" int forge_stub_launches(void) { return g_launches.load(); }

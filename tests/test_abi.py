@@ -165,6 +165,26 @@ def test_one_launch_backward_validation(forge):
                                         1, 1, None, None) == 2
 
 
+def test_no_alloc_backward_validation(forge):
+    """The allocation-free variant: the one-launch checks, and K within its static counters
+    ((4096 - 26) x 128 columns)."""
+    f = forge
+    GB = 1 << 30
+    r = ctypes.byref
+    L = f._lib()
+    h = f._hyper(synth.default_hyper("sgd"))
+    T, N = 1, 256
+    Kmax = (4096 - 26) * 128
+
+    def call(K, n=N):
+        return L.forge_linear_backward_step_fused_noalloc(
+            r(_t(f, T, K, f.BF16)), r(_t(f, T, n, f.BF16, GB)), r(_t(f, n, K, f.BF16, 2 * GB)),
+            r(_t(f, T, K, f.BF16, 3 * GB)), None, None, r(h), 6, 1, 1, None, None)
+
+    assert call(Kmax + 128) == 2 and "allocation-free" in f.last_error()
+    assert call(1024, n=128) == 2                                         # N % 256
+
+
 @pytest.mark.parametrize("opt", synth.OPTIMIZERS)
 @pytest.mark.parametrize("t", [1, 2, 5, 6, 50])
 def test_host_scalars_match_oracle(forge, opt, t):
