@@ -13,7 +13,7 @@
 //     where they fill whole rounds, the remaining columns in a second 256 x 128 launch;
 //   * fp8 e4m3 inputs: the same tiles with 8-bit transpose reads (forge_mainloop8.h);
 //   * fp32 inputs and layers with too few tiles: 128 x 128 tiles staged through registers
-//     (forge_mainloop.h).
+//     (forge_mainloop.h), 64 x 64 for fp32 layers with fewer 128 x 128 tiles than CUs.
 // The element-wise update of a 16-element segment (forge_device.h) is shared by all of them.
 //
 // Unfused baseline (Technical Summary section 1 "The Problem"): the same contraction writes
@@ -22,7 +22,8 @@
 //
 // dgrad: dX = dY W on the LDS-DMA path (256-token x 256-column tiles in one 8-wave workgroup
 // per CU where K % 256 == 0 and they fill the CUs, else 256 x 128), run before the step so
-// that it sees the old weight (Technical Summary section 5, limitations).
+// that it sees the old weight (Technical Summary section 5, limitations).  The same dgrad and
+// step in one launch: forge_backward.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

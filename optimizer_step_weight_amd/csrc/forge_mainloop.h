@@ -1,4 +1,5 @@
-// forge_mainloop.h -- the token contraction of one 128 x 128 weight tile on gfx950.
+// forge_mainloop.h -- the token contraction of one S x S weight tile on gfx950 (S = 128, or 64
+// for fp32 layers with fewer 128 x 128 tiles than CUs).
 //
 // FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism": for one
 // tile of W the kernel accumulates the products of the upstream gradient dY and the input
@@ -16,10 +17,11 @@
 // argument: only the order of the sum over tokens differs), so the token order inside an LDS
 // row need only be the same for the dY and X panels, which it is by construction.
 //
-// Workgroup: 256 threads = 4 waves of 64; the 128 x 128 tile is split 2 x 2 into 64 x 64
-// wave tiles of 4 x 4 MFMA 16x16 blocks.  Accumulator layout (16x16 MFMA output): lane l,
-// register r of block (i, j) holds W row 16 i + 4 (l / 16) + r and column 16 j + (l % 16) of
-// the wave tile.
+// Workgroup: 256 threads = 4 waves of 64; the S x S tile is split 2 x 2 into S/2 x S/2 wave
+// tiles of (S/32) x (S/32) MFMA 16x16 blocks (4 x 4 for S = 128, 2 x 2 for S = 64; with
+// S = 64 half of the loading threads fetch a slab, and four workgroups share a CU).  Accumulator
+// layout (16x16 MFMA output): lane l, register r of block (i, j) holds W row 16 i + 4 (l / 16)
+// + r and column 16 j + (l % 16) of the wave tile.
 #pragma once
 
 #include <hip/hip_runtime.h>
