@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import synth
-from oracle import numerics, wgrad
+from oracle import numerics, optimizers, wgrad
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -110,6 +110,38 @@ def test_one_launch_equals_two_launches(lib, opt, state_fmt, Tn, Nn, Kn):
                 assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1]), name
             else:
                 assert np.array_equal(x, y), name
+
+
+# every rule and moment format, bitwise against the two-launch path (2048 x 2048: 128 tiles of
+# 256 x 128, the smallest layer on which both paths use them)
+ALL = [(o, f) for o in synth.OPTIMIZERS for f in ("f32", "int8", "int8dyn")
+       if f == "f32" or optimizers.STATES[o]]
+
+
+@pytest.mark.parametrize("opt,state_fmt", ALL, ids=["-".join(c) for c in ALL])
+def test_one_launch_every_rule_equals_two_launches(lib, opt, state_fmt):
+    _say("one-launch vs two launches, every rule", opt, state_fmt)
+    Tn, Nn, Kn = 200, 2048, 2048
+    rng = np.random.default_rng(107)
+    h = synth.default_hyper(opt)
+    W = synth.random_weight(108, Nn, Kn, "bf16")
+    m, v = P.init_states(opt, state_fmt, rng, Nn, Kn)
+    X, dY = synth.gaussian_case(450, Tn, Nn, Kn, "bf16")
+    a = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    b = P.DeviceStep(W, m, v, "bf16", state_fmt)
+    dXa = torch.empty((Tn, Kn), dtype=torch.bfloat16, device="cuda")
+    dXb = torch.empty((Tn, Kn), dtype=torch.bfloat16, device="cuda")
+    ws = _run(lib, True, X, dY, a, dXa, opt, h, 3, 9)
+    _run(lib, False, X, dY, b, dXb, opt, h, 3, 9)
+    assert _error_word(ws) == 0
+    assert torch.equal(dXa.view(torch.int16), dXb.view(torch.int16)), "dX"
+    for x, y, name in zip(a.host(), b.host(), ("W", "m", "v")):
+        if x is None:
+            continue
+        if isinstance(x, tuple):
+            assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1]), name
+        else:
+            assert np.array_equal(x, y), name
 
 
 @pytest.mark.parametrize("Tn", [0, 1, 255, 256, 257])
