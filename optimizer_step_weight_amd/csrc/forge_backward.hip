@@ -34,44 +34,36 @@ static __device__ __align__(256) int scratch[forge::kBackwardScratchWords];
 namespace forge {
 
 // Workspace words: [1] the error word; [2 + 8 p + q] claims made on queue q of phase p
-// (0: dX tiles, 1: full step tiles, 2: half step tiles); [26 + kb] dX tiles of column block kb
-// that have finished reading W.
-enum : int { BWD_ERROR = 1, BWD_QUEUES = 2, BWD_DONE = 26 };
-constexpr int kQueues = 8, kPhases = 3;
+// (0: dX tiles, 1: full step tiles, 2: half step tiles; forge_plan.h); [26 + kb] dX tiles of
+// column block kb that have finished reading W.
+enum : int { BWD_ERROR = 1, BWD_QUEUES = 2, BWD_DONE = BWD_QUEUES + plan::kPhases * plan::kQueues };
 constexpr int kClaimAttempts = 64;
-
-__device__ __forceinline__ int queue_size(int n, int q) { return n / kQueues + (q < n % kQueues ? 1 : 0); }
 
 // Wave 0 claims the workgroup's item: phase and index within the phase (-1 if none is left,
 // which only overlapping calls on one workspace can cause).  One snapshot of the 24 queue
-// counters (lane l reads counter l) picks the earliest phase with an open queue and in it the
-// workgroup's own queue or the next open one; an atomic add claims an item there, or, if
-// others emptied that queue meanwhile, the snapshot is taken again.  Counters only grow, so a
-// queue seen full is empty for good.
+// counters (lane l reads counter l) picks the queue (plan::pick_queue); an atomic add claims an
+// item there, or, if others used up that queue meanwhile, the snapshot is taken again.  Counters
+// only grow, so a queue seen used up stays so.
 __device__ __forceinline__ void claim_item(const BackwardArgs& b, const GemmArgs& g, int& phase, int& index) {
-  const int lane = (int)(threadIdx.x & 63), q0 = (int)(blockIdx.x & (kQueues - 1));
-  const int n_half = 2 * g.nbn * (g.nbk - g.kb_split);
-  const int lp = lane / kQueues, lq = lane % kQueues;
-  const int ln = lp == 0 ? b.n_dgrad : lp == 1 ? g.nfull : n_half;
+  const int lane = (int)(threadIdx.x & 63), q0 = (int)(blockIdx.x & (plan::kQueues - 1));
+  const plan::BackwardItems it = plan::backward_items(g, b.nbT);
+  const int ln = plan::phase_items(it, lane / plan::kQueues);
+  const bool counter_lane = lane < plan::kPhases * plan::kQueues;
   phase = -1;
   index = -1;
   for (int attempt = 0; attempt < kClaimAttempts; ++attempt) {
     int c = 0;
-    if (lane < kPhases * kQueues)
-      c = __hip_atomic_load(b.ctr + BWD_QUEUES + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t open = __ballot(lane < kPhases * kQueues && c < queue_size(ln, lq));
-    if (open == 0) return;
-    const int p = (int)(__builtin_ctzll(open) / kQueues);
-    const uint32_t pm = (uint32_t)(open >> (kQueues * p)) & 0xFFu;
-    const uint32_t rot = ((pm >> q0) | (pm << (kQueues - q0))) & 0xFFu;
-    const int q = (q0 + __builtin_ctz(rot)) & (kQueues - 1);
+    if (counter_lane) c = __hip_atomic_load(b.ctr + BWD_QUEUES + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t open = (uint32_t)__ballot(counter_lane && c < plan::queue_size(ln, lane % plan::kQueues));
+    int p, q;
+    if (!plan::pick_queue(open, q0, p, q)) return;
     int k = 0;
-    if (lane == 0) k = atomicAdd(b.ctr + BWD_QUEUES + kQueues * p + q, 1);
+    if (lane == 0) k = atomicAdd(b.ctr + BWD_QUEUES + plan::kQueues * p + q, 1);
     k = __shfl(k, 0);
-    const int n = p == 0 ? b.n_dgrad : p == 1 ? g.nfull : n_half;
-    if (k < queue_size(n, q)) {
+    const int item = plan::claimed_item(plan::phase_items(it, p), q, k);
+    if (item >= 0) {
       phase = p;
-      index = q + kQueues * k;
+      index = item;
       return;
     }
   }

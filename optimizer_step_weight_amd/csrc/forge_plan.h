@@ -180,5 +180,42 @@ inline int plan_launches(int in_type, const GemmArgs& g, int cus, int fused, Lau
   return n;
 }
 
+// ---- work queues of the one-launch backward step (forge_backward.hip)
+// Three phases of work items, in order: 0 the dX tiles, 1 the step's full tiles, 2 its half
+// tiles.  Each phase is spread over 8 queues, one per XCD slot: the k-th claim on queue q of a
+// phase returns its item q + 8 k while k < queue_size(n, q), so the items a queue hands out are
+// those the separate launches give workgroups q, q + 8, q + 16, ... of the XCD q.
+constexpr int kQueues = 8, kPhases = 3;
+
+struct BackwardItems {
+  int dgrad, full, half;  // items per phase
+};
+__host__ __device__ inline BackwardItems backward_items(const GemmArgs& g, int nbT) {
+  return BackwardItems{nbT * g.nbk, g.nfull, 2 * g.nbn * (g.nbk - g.kb_split)};
+}
+__host__ __device__ inline int phase_items(const BackwardItems& it, int p) {
+  return p == 0 ? it.dgrad : p == 1 ? it.full : it.half;
+}
+__host__ __device__ inline int queue_size(int n, int q) { return n / kQueues + (q < n % kQueues ? 1 : 0); }
+
+// The queue a workgroup of XCD slot q0 claims from, given which queues were open (bit 8 p + q of
+// `open` set: claims on queue q of phase p had not yet used up its items) in one snapshot of the
+// claim counters: the earliest phase with an open queue, and in it queue q0 or the next open one
+// after it.  False if no queue was open.
+__host__ __device__ inline bool pick_queue(uint32_t open, int q0, int& phase, int& queue) {
+  if (open == 0) return false;
+  phase = __builtin_ctz(open) / kQueues;
+  const uint32_t pm = (open >> (kQueues * phase)) & 0xFFu;
+  const uint32_t rot = ((pm >> q0) | (pm << (kQueues - q0))) & 0xFFu;
+  queue = (q0 + __builtin_ctz(rot)) & (kQueues - 1);
+  return true;
+}
+
+// The item the k-th claim on queue q of a phase of n items returns, or -1 once the queue's items
+// are used up.
+__host__ __device__ inline int claimed_item(int n, int q, int k) {
+  return k < queue_size(n, q) ? q + kQueues * k : -1;
+}
+
 }  // namespace plan
 }  // namespace forge
