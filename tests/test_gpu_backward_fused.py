@@ -1,6 +1,6 @@
 """GPU parity of the one-launch backward step (forge_linear_backward_step_fused): dX from the
-weight before the step and the fused step, in one grid of dX tiles and step tiles handed out
-by ticket.
+weight before the step and the fused step, in one grid of dX tiles and step tiles taken from
+per-XCD-slot work queues.
 
   * against the oracle: exact-sum X and dY (the gradient is exact, so W, m, v meet the plain
     bar), dX within one bf16 ULP plus the fp32 summation bound of its N products;
