@@ -64,24 +64,31 @@ __global__ __launch_bounds__(ml2::THREADS, kOcc2) void fused_step_kernel2(GemmAr
 // bf16 inputs, 256 x 256 tiles, one workgroup of 8 waves per CU (forge_mainloop2.h, wide
 // tiles): both 128-column halves share the dY panel and 4 slabs fit in LDS.  The epilogue is
 // the 256 x 128 tile's, run by each half: threads 0-255 update columns k0 .. k0 + 127 and
-// threads 256-511 columns k0 + 128 .. k0 + 255, each staging through its own LDS buffer.  The
-// launch covers the nbn row blocks from nb_base on and the nbk / 2 wide column blocks from
-// kb_base / 2 on.
+// threads 256-511 columns k0 + 128 .. k0 + 255, each staging through its own LDS buffer.  A
+// launch may also hold 128 x 256 half-wide tiles, whose halves run the 128 x 128 tile's
+// epilogue (plan::wide_item gives each workgroup its tile).
 constexpr int kSmemW = ml2::WidePipe::SMEM > 2 * ml2::EPI_BYTES ? ml2::WidePipe::SMEM : 2 * ml2::EPI_BYTES;
-static_assert(kSmemW <= 160 * 1024, "wide tiles fit the CU's LDS");
+static_assert(kSmemW <= 160 * 1024 && ml2::WideHalfPipe::SMEM <= kSmemW, "wide tiles fit the CU's LDS");
 
 template <int WT, int ST, int OPT>
 __global__ __launch_bounds__(2 * ml2::THREADS, 1) void fused_step_kernel2w(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemW];
   int n0, kw0;
-  plan::wide_tile(g, (int)blockIdx.x, n0, kw0);
+  const bool half = plan::wide_item(g, (int)blockIdx.x, n0, kw0);
   const int kh = (int)(threadIdx.x >> 8);
-  ml2::floatx4 acc[8][4];
-  ml2::contract_wide(acc, smem, g, n0, kw0);
   unsigned char* mine = smem + kh * ml2::EPI_BYTES;
   float* st = reinterpret_cast<float*>(mine);
-  tile_epilogue<OPT, WT, ST, 2, true>(g, e, mine, n0, kw0 + kh * ml2::BN,
-                                      [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
+  if (half) {
+    ml2::floatx4 acc[4][4];
+    ml2::contract_wide<ml2::WideHalfPipe>(acc, smem, g, n0, kw0);
+    tile_epilogue<OPT, WT, ST, 1, true>(g, e, mine, n0, kw0 + kh * ml2::BN,
+                                        [&](int) { ml2::stage_acc_all(st, acc, 1.0f); });
+  } else {
+    ml2::floatx4 acc[8][4];
+    ml2::contract_wide<ml2::WidePipe>(acc, smem, g, n0, kw0);
+    tile_epilogue<OPT, WT, ST, 2, true>(g, e, mine, n0, kw0 + kh * ml2::BN,
+                                        [&](int h) { ml2::stage_acc_half(st, acc, 1.0f, h); });
+  }
 }
 
 template <int ST>

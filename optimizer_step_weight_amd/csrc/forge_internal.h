@@ -60,6 +60,11 @@ struct GemmArgs {
   // [0, nfull) take 256 x 128 tiles of column blocks [0, kb_split) of that range and the rest
   // 128 x 128 tiles of column blocks [kb_split, nbk).
   int nfull = 0, kb_split = 0, kb_base = 0, nbk = 0, nb_base = 0, nbn = 0;
+  // Wide launches on bf16 inputs (forge_plan.h, wide_item): the nfull 256 x 256 tiles cover
+  // the nbn row blocks from nb_base on and the kb_split column blocks from kb_base on; the
+  // 128 x 256 half-wide tiles cover the hn row blocks from h_nb on and the hk column blocks
+  // from h_kb on, nfront of them dispatched before the wide tiles and the rest after.
+  int nfront = 0, h_nb = 0, hn = 0, h_kb = 0, hk = 0;
 };
 
 // Launchers (defined in the .hip translation units).  Return a hipError_t as int.

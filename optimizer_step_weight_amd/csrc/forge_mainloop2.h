@@ -222,87 +222,108 @@ __device__ __forceinline__ void contract(floatx4 (&acc)[P::MB][4], unsigned char
 // One workgroup of 8 waves contracts a 256 x 256 tile: waves 0-3 the columns k0 .. k0 + 127
 // and waves 4-7 the columns k0 + 128 .. k0 + 255, each group with the wave layout of the
 // 256 x 128 tile above.  Both groups read the same dY panel, so a slab moves 16 KiB of dY and
-// 16 KiB of X (one third less than two 256 x 128 tiles), and 4 stages fit in 128 KiB.  Every
-// element's sum runs over the tokens in the same slab and k-slot order as on the 256 x 128
-// path, so both give bitwise the same gradient.
-struct WidePipe {
-  static constexpr int TK = 32, STAGES = 4, ROW = 512;   // 256 bf16 per token row, both panels
-  static constexpr int PANEL = TK * ROW, STAGE = 2 * PANEL, SMEM = STAGES * STAGE;
-  static constexpr int DMA = 4;                         // per wave per slab: 2 of dY, 2 of X
+// 16 KiB of X (one third less than two 256 x 128 tiles), and 4 stages fit in 128 KiB.
+// Half-wide tiles (128 x 256, MB = 4) have the same layout with the half tile's 64 x 64 wave
+// tiles: 8 KiB of dY and 16 KiB of X per slab.  Every element's sum runs over the tokens in
+// the same slab and k-slot order as on the 256 x 128 path, so all give bitwise the same
+// gradient.
+template <int MB_>
+struct WidePipeT {
+  static constexpr int MB = MB_, TK = 32, STAGES = 4;
+  static constexpr int ROW_A = 64 * MB, ROW_B = 512;  // bytes per dY / X token row in LDS
+  static constexpr int PANEL_A = TK * ROW_A, PANEL_B = TK * ROW_B;
+  static constexpr int STAGE = PANEL_A + PANEL_B, SMEM = STAGES * STAGE;
+  static constexpr int DMA_A = PANEL_A / 8192, DMA_B = PANEL_B / 8192;  // 1 KiB copies per wave per slab
+  static constexpr int DMA = DMA_A + DMA_B;
+  static constexpr int CPR_A = ROW_A / 16, RPD_A = 64 / CPR_A;  // 16-byte chunks per dY row, rows per copy
+  static_assert(MB == 8 || MB == 4, "tile height");
 };
+using WidePipe = WidePipeT<8>;
+using WideHalfPipe = WidePipeT<4>;
 
+template <class P>
 struct WideFeed {
   u32x4 rA, rB;
-  uint32_t offA[2], offB[2];
+  uint32_t offA[P::DMA_A], offB[P::DMA_B];
   uint32_t stepA, stepB;
 };
 
-// A 1 KiB DMA covers 2 token rows of 512 bytes (32 chunks of 16 bytes); wave w moves rows
-// 4 w .. 4 w + 3 of each panel.  Chunks are XOR-swizzled with 2 (t mod 8) as above.
-__device__ __forceinline__ void make_wide_feed(WideFeed& f, const GemmArgs& g, int n0, int k0) {
+// A 1 KiB copy covers RPD_A dY rows (2 of 512 bytes, or 4 of 256 bytes for half-wide tiles)
+// or 2 X rows of 512 bytes; wave w moves dY rows RPD_A d .. (d = DMA_A w + j) and X rows
+// 2 x, 2 x + 1 (x = 2 w + j).  Chunks are XOR-swizzled with 2 (t mod 8) as above.
+template <class P>
+__device__ __forceinline__ void make_wide_feed(WideFeed<P>& f, const GemmArgs& g, int n0, int k0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f.rA = make_rsrc(g.dY, (uint32_t)(g.T * g.N * 2));
   f.rB = make_rsrc(g.X, (uint32_t)(g.T * g.K * 2));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 2 * (2 * wave + j) + (lane >> 5), c = (lane & 31) ^ swz(r);
+  for (int j = 0; j < P::DMA_A; ++j) {
+    const int d = P::DMA_A * wave + j, r = P::RPD_A * d + lane / P::CPR_A, c = (lane % P::CPR_A) ^ swz(r);
     f.offA[j] = (uint32_t)(r * g.N * 2 + n0 * 2 + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < P::DMA_B; ++j) {
+    const int r = 2 * (P::DMA_B * wave + j) + (lane >> 5), c = (lane & 31) ^ swz(r);
     f.offB[j] = (uint32_t)(r * g.K * 2 + k0 * 2 + c * 16);
   }
-  f.stepA = (uint32_t)(WidePipe::TK * g.N * 2);
-  f.stepB = (uint32_t)(WidePipe::TK * g.K * 2);
+  f.stepA = (uint32_t)(P::TK * g.N * 2);
+  f.stepB = (uint32_t)(P::TK * g.K * 2);
 }
 
-__device__ __forceinline__ void wide_issue(const WideFeed& f, unsigned char* stage, int slab) {
+template <class P>
+__device__ __forceinline__ void wide_issue(const WideFeed<P>& f, unsigned char* stage, int slab) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t sa = (uint32_t)slab * f.stepA, sb = (uint32_t)slab * f.stepB;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) dma16(f.rA, f.offA[j] + sa, stage + (2 * wave + j) * 1024);
+  for (int j = 0; j < P::DMA_A; ++j) dma16(f.rA, f.offA[j] + sa, stage + (P::DMA_A * wave + j) * 1024);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) dma16(f.rB, f.offB[j] + sb, stage + WidePipe::PANEL + (2 * wave + j) * 1024);
+  for (int j = 0; j < P::DMA_B; ++j) dma16(f.rB, f.offB[j] + sb, stage + P::PANEL_A + (P::DMA_B * wave + j) * 1024);
 }
 
-// The 256 x 128 tile's slab step on 512-byte rows; kh selects the 128-column half of X.
-__device__ __forceinline__ void wide_mma_stage(floatx4 (&acc)[8][4], const unsigned char* stage, int wm, int wn,
+// The 256 x 128 (or 128 x 128) tile's slab step on 512-byte X rows; kh selects the 128-column
+// half of X.
+template <class P>
+__device__ __forceinline__ void wide_mma_stage(floatx4 (&acc)[P::MB][4], const unsigned char* stage, int wm, int wn,
                                                int kh) {
   const int lane = threadIdx.x & 63, q = lane >> 4, i = lane & 15;
   const unsigned char* pa = stage;
-  const unsigned char* pb = stage + WidePipe::PANEL;
+  const unsigned char* pb = stage + P::PANEL_A;
   const int r0 = 4 * q + (i >> 2), r1 = r0 + 16;
   bf16x8 b[4];
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, WidePipe::ROW, r0, r1, kh * 128 + wn * 64 + 16 * bj, i);
+  for (int bj = 0; bj < 4; ++bj) b[bj] = frag(pb, P::ROW_B, r0, r1, kh * 128 + wn * 64 + 16 * bj, i);
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi) {
-    const bf16x8 a = frag(pa, WidePipe::ROW, r0, r1, a_row<8>(wm, bi), i);
+  for (int bi = 0; bi < P::MB; ++bi) {
+    const bf16x8 a = frag(pa, P::ROW_A, r0, r1, a_row<P::MB>(wm, bi), i);
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[bj], acc[bi][bj], 0, 0, 0);
   }
 }
 
-// acc = this wave's part of dW for the 256 x 256 tile at (n0, k0).  Ends with a barrier.
-__device__ __forceinline__ void contract_wide(floatx4 (&acc)[8][4], unsigned char* smem, const GemmArgs& g, int n0,
+// acc = this wave's part of dW for the 256 x 256 (or 128 x 256) tile at (n0, k0).  Ends with
+// a barrier.
+template <class P>
+__device__ __forceinline__ void contract_wide(floatx4 (&acc)[P::MB][4], unsigned char* smem, const GemmArgs& g, int n0,
                                               int k0) {
-  using P = WidePipe;
   const int wave = threadIdx.x >> 6, kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi)
+  for (int bi = 0; bi < P::MB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = floatx4{0.f, 0.f, 0.f, 0.f};
-  WideFeed f;
-  make_wide_feed(f, g, n0, k0);
+  WideFeed<P> f;
+  make_wide_feed<P>(f, g, n0, k0);
   const int nsl = (int)((g.T + P::TK - 1) / P::TK);
 #pragma unroll
   for (int s = 0; s < P::STAGES - 1; ++s)
-    if (s < nsl) wide_issue(f, smem + s * P::STAGE, s);
+    if (s < nsl) wide_issue<P>(f, smem + s * P::STAGE, s);
   for (int s = 0; s < nsl; ++s) {
     const int ahead = min(nsl - 1 - s, P::STAGES - 2);
     if (ahead >= 2) wait_vm<2 * P::DMA>();
     else if (ahead == 1) wait_vm<P::DMA>();
     else wait_vm<0>();
     barrier();
-    if (s + P::STAGES - 1 < nsl) wide_issue(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
-    wide_mma_stage(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn, kh);
+    if (s + P::STAGES - 1 < nsl) wide_issue<P>(f, smem + ((s + P::STAGES - 1) % P::STAGES) * P::STAGE, s + P::STAGES - 1);
+    wide_mma_stage<P>(acc, smem + (s % P::STAGES) * P::STAGE, wm, wn, kh);
   }
   barrier();
 }
@@ -326,9 +347,10 @@ __device__ __forceinline__ void stage_acc_half(float* st, const floatx4 (&acc)[8
   }
 }
 
-// Stage all 128 rows of a half tile's accumulators in LDS as fp32 [128][EPI_LD], times `scale`.
+// Stage all 128 rows of a half tile's accumulators in LDS as fp32 [128][EPI_LD], times `scale`
+// (in an 8-wave workgroup, each group of 4 waves into its own buffer).
 __device__ __forceinline__ void stage_acc_all(float* st, const floatx4 (&acc)[4][4], float scale) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)

@@ -51,7 +51,24 @@ __host__ __device__ inline void half_tile(const GemmArgs& g, int hb, int& n0, in
   n0 = g.nb_base * kRows + nb * kHalfRows;
   k0 = (g.kb_base + g.kb_split + kb) * kCols;
 }
-// 256 x 256 tile b of a wide launch (columns k0 .. k0 + 255).
+// Workgroup b of a bf16 wide launch: the origin of its tile, and whether that tile is a
+// 128 x 256 half-wide one (the first nfront workgroups and those after the nfull wide tiles)
+// rather than 256 x 256 (columns k0 .. k0 + 255 either way).
+__host__ __device__ inline bool wide_item(const GemmArgs& g, int b, int& n0, int& k0) {
+  int nb, kb;
+  const int w = b - g.nfront;
+  if (w >= 0 && w < g.nfull) {
+    tile_coords_at(w, g.nbn, g.kb_split / 2, nb, kb);
+    n0 = (g.nb_base + nb) * kRows;
+    k0 = (g.kb_base + 2 * kb) * kCols;
+    return false;
+  }
+  tile_coords_at(w < 0 ? b : b - g.nfull, 2 * g.hn, g.hk / 2, nb, kb);
+  n0 = g.h_nb * kRows + nb * kHalfRows;
+  k0 = (g.h_kb + 2 * kb) * kCols;
+  return true;
+}
+// 256 x 256 tile b of an fp8 wide launch (columns k0 .. k0 + 255).
 __host__ __device__ inline void wide_tile(const GemmArgs& g, int b, int& n0, int& k0) {
   int nb, kb;
   tile_coords_at(b, g.nbn, g.nbk / 2, nb, kb);
@@ -92,21 +109,45 @@ inline unsigned plan_split(GemmArgs& g, int slots) {
   return (unsigned)(g.nfull + 2 * nbN * c);
 }
 
-// Wide 256 x 256 tiles for long token counts (T >= 8192, where the faster contraction outweighs
-// the epilogue that no other workgroup on the CU overlaps; at T = 4096 both layouts take the same
-// time), in whole rounds of one workgroup per CU.  Either the first kw 256-column blocks of every
-// 256-row block, kw the largest count for which N / 256 * kw is a positive multiple of the CU
-// count, or, where no column count works and K is a multiple of 256, the first nw 256-row blocks
-// over all columns, nw the largest such count of rows.  The rest of the weight runs on the
-// 256 x 128 path.
+// Wide 256 x 256 tiles in one workgroup of 8 waves per CU: a faster contraction than two
+// 256 x 128 workgroups, but no other workgroup on the CU overlaps a tile's epilogue.  A wide
+// launch should end in whole rounds.
+//  * bf16 inputs, T >= 4096, every tile wide (K % 256 == 0) and R wide tiles leaving
+//    R mod C = r over the C CUs: the last r / (N / 256) 256-column blocks (or the last
+//    r / (K / 256) row blocks), whichever divides, become 2 r half-wide tiles of 128 x 256 in
+//    the same launch.  Half of them go first, the rest after the wide tiles: the CUs that
+//    start on a half-wide tile then run half a tile out of phase with the others, so the
+//    epilogues' streams of W, m and v do not all fall in the same interval (at down_proj,
+//    T = 4096: 567 us against 582 us with all half-wide tiles last, and 600 us on 256 x 128
+//    tiles).
+//  * Otherwise, for T >= 8192 (where the faster contraction outweighs the unoverlapped
+//    epilogue; at T = 4096 the two tied): the first kw 256-column blocks of every row block,
+//    kw the largest count for which N / 256 * kw is a positive multiple of the CU count, or,
+//    where no column count works and K is a multiple of 256, the first nw row blocks over all
+//    columns, nw the largest such count; the rest of the weight runs on the 256 x 128 path.
+//    fp8 inputs only take this form.
+constexpr int64_t kWideHalvesMinT = 4096, kWideMinT = 8192;
 struct WidePlan {
-  int kw = 0, nw = 0;
+  int kw = 0, nw = 0;  // whole rounds on part of the weight
+  int hc = 0, hr = 0;  // bf16: the whole weight, the last hc column or hr row blocks half-wide
 };
 
-inline WidePlan plan_wide(const GemmArgs& g, int cus) {
+inline WidePlan plan_wide(const GemmArgs& g, int cus, bool halves) {
   WidePlan p;
-  if (g.T < 8192 || cus <= 0) return p;
+  if (g.T < kWideHalvesMinT || cus <= 0) return p;
   const int nbN = (int)(g.N / kRows), nbK2 = (int)(g.K / (2 * kCols));
+  if (halves && g.K % (2 * kCols) == 0 && nbN * nbK2 > cus) {
+    const int r = (nbN * nbK2) % cus;
+    if (r > 0 && r % nbN == 0) {
+      p.hc = r / nbN;
+      return p;
+    }
+    if (r > 0 && r % nbK2 == 0) {
+      p.hr = r / nbK2;
+      return p;
+    }
+  }
+  if (g.T < kWideMinT) return p;
   for (int kw = nbK2; kw > 0; --kw)
     if ((nbN * kw) % cus == 0) {
       p.kw = kw;
@@ -156,7 +197,23 @@ inline int plan_launches(int in_type, const GemmArgs& g, int cus, int fused, Lau
   if (use_v2(in_type, g) || use_v8(in_type, g)) {
     const int kind = use_v2(in_type, g) ? LAUNCH_V2 : LAUNCH_V8;
     GemmArgs rest = whole_dma(g);
-    const WidePlan wp = fused ? plan_wide(g, cus) : WidePlan{};
+    const WidePlan wp = fused ? plan_wide(g, cus, kind == LAUNCH_V2) : WidePlan{};
+    if (wp.hc > 0 || wp.hr > 0) {  // the whole weight in one launch with half-wide tiles
+      GemmArgs w = rest;
+      if (wp.hc > 0) {
+        w.kb_split = w.nbk - 2 * wp.hc;
+        w.h_nb = 0, w.hn = w.nbn, w.h_kb = w.kb_split, w.hk = 2 * wp.hc;
+      } else {
+        w.nbn -= wp.hr;
+        w.kb_split = w.nbk;
+        w.h_nb = w.nbn, w.hn = wp.hr, w.h_kb = 0, w.hk = w.nbk;
+      }
+      w.nfull = w.nbn * (w.kb_split / 2);
+      const int nhalf = w.hn * w.hk;
+      w.nfront = (nhalf / 2) & ~7;
+      out[n++] = Launch{LAUNCH_WIDE, w, (unsigned)(w.nfull + nhalf), 0};
+      return n;
+    }
     if (wp.kw > 0 || wp.nw > 0) {
       GemmArgs wide = rest;
       if (wp.kw > 0) {
@@ -168,7 +225,9 @@ inline int plan_launches(int in_type, const GemmArgs& g, int cus, int fused, Lau
         rest.nb_base = wp.nw;
         rest.nbn -= wp.nw;
       }
-      out[n++] = Launch{LAUNCH_WIDE, wide, (unsigned)(wide.nbn * (wide.nbk / 2)), 0};
+      wide.kb_split = wide.nbk;
+      wide.nfull = wide.nbn * (wide.nbk / 2);
+      out[n++] = Launch{LAUNCH_WIDE, wide, (unsigned)wide.nfull, 0};
       if (rest.nbn == 0 || rest.nbk == 0) return n;
     }
     const unsigned grid = kind == LAUNCH_V2 ? plan_split(rest, 2 * cus) : (unsigned)(rest.nbn * rest.nbk);

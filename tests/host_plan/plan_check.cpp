@@ -47,9 +47,18 @@ static void check(int in_type, long N, long K, long T, int cus, int fused) {
       long rows = 0, cols = 0;
       switch (L[i].kind) {
         case LAUNCH_WIDE:
-          CHECK(fused && a.nbk % 2 == 0 && L[i].grid == (unsigned)(a.nbn * (a.nbk / 2)), "bad wide launch");
-          wide_tile(a, (int)b, n0, k0);
-          rows = kRows, cols = 2 * kCols;
+          if (in_type == FORGE_IN_BF16) {
+            CHECK(fused && a.kb_split % 2 == 0 && a.hk % 2 == 0 && a.nfull == a.nbn * (a.kb_split / 2) &&
+                      L[i].grid == (unsigned)(a.nfull + a.hn * a.hk) && a.nfront >= 0 && a.nfront <= a.hn * a.hk,
+                  "bad wide launch");
+            const bool half = wide_item(a, (int)b, n0, k0);
+            rows = half ? kHalfRows : kRows, cols = 2 * kCols;
+          } else {
+            CHECK(fused && a.nbk % 2 == 0 && a.hn == 0 && L[i].grid == (unsigned)(a.nbn * (a.nbk / 2)),
+                  "bad wide launch");
+            wide_tile(a, (int)b, n0, k0);
+            rows = kRows, cols = 2 * kCols;
+          }
           break;
         case LAUNCH_V2:
           if ((int)b < a.nfull) full_tile(a, (int)b, n0, k0), rows = kRows, cols = kCols;
@@ -97,18 +106,53 @@ int main() {
             check(in, s[0], s[1], T, cus, fused);
             ++cases;
           }
-  // the wide plans taken at 256 CUs for the Llama-3.1-8B shapes at T = 8192
+  // the wide plans taken at 256 CUs for the Llama-3.1-8B shapes at T = 8192: bf16 puts the
+  // whole weight in one launch with one round of half-wide tiles (the last 8 row blocks of
+  // gate/up, the last 8 256-column blocks of down_proj), fp8 keeps whole rounds of wide tiles
+  // on part of the weight
   GemmArgs g{};
   g.T = 8192;
   g.N = 14336;
   g.K = 4096;
-  const WidePlan a = plan_wide(g, 256);
+  const WidePlan a = plan_wide(g, 256, true), a8 = plan_wide(g, 256, false);
   g.N = 4096;
   g.K = 14336;
-  const WidePlan b = plan_wide(g, 256);
-  if (!(a.kw == 0 && a.nw == 48 && b.kw == 48 && b.nw == 0)) {
-    std::fprintf(stderr, "unexpected wide plans: gate (%d, %d), down (%d, %d)\n", a.kw, a.nw, b.kw, b.nw);
+  const WidePlan b = plan_wide(g, 256, true), b8 = plan_wide(g, 256, false);
+  if (!(a.hr == 8 && a.hc == 0 && b.hc == 8 && b.hr == 0 && a8.nw == 48 && a8.kw == 0 && b8.kw == 48 && b8.nw == 0)) {
+    std::fprintf(stderr, "unexpected wide plans: gate (%d, %d, %d), down (%d, %d, %d)\n", a.hr, a8.nw, a8.kw, b.hc,
+                 b8.kw, b8.nw);
     ++g_fail;
+  }
+  // down_proj at T = 4096 and 8192: one launch of 768 wide tiles between two runs of 128
+  // half-wide tiles; at T = 4096 a weight whose wide tiles fill whole rounds (4096 x 4096), and
+  // fp8 inputs, stay on the 256 x 128 path
+  for (long T : {4096L, 8192L}) {
+    Launch L[2];
+    g.T = T;
+    g.N = 4096;
+    g.K = 14336;
+    int n = plan_launches(FORGE_IN_BF16, g, 256, 1, L);
+    if (!(n == 1 && L[0].kind == LAUNCH_WIDE && L[0].g.nfull == 768 && L[0].g.hn * L[0].g.hk == 256 &&
+          L[0].grid == 1024 && L[0].g.nfront == 128)) {
+      std::fprintf(stderr, "unexpected down_proj wide launch at T = %ld\n", T);
+      ++g_fail;
+    }
+    n = plan_launches(FORGE_IN_FP8, g, 256, 1, L);
+    if (T == 4096 && !(n == 1 && L[0].kind == LAUNCH_V8)) {
+      std::fprintf(stderr, "fp8 down_proj at T = 4096 took wide tiles\n");
+      ++g_fail;
+    }
+  }
+  {
+    Launch L[2];
+    g.T = 4096;
+    g.N = 4096;
+    g.K = 4096;
+    const int n = plan_launches(FORGE_IN_BF16, g, 256, 1, L);
+    if (!(n == 1 && L[0].kind == LAUNCH_V2)) {
+      std::fprintf(stderr, "4096 x 4096 at T = 4096 took wide tiles\n");
+      ++g_fail;
+    }
   }
   std::printf("plan_check: %d cases, %d failures\n", cases, g_fail);
   return g_fail ? 1 : 0;

@@ -1,10 +1,11 @@
 """GPU parity on whole tensors at the workloads' real shapes and launch configurations.
 
 The library is called as the benchmark calls it, so every tile path of the timed launches is
-covered: the Llama-3.1-8B down_proj at T = 4096 (1536 256 x 128 tiles and 512 128 x 128 half
-tiles in one launch), the 256 x 256 wide tiles at T = 8192 (alone for q_proj, followed by a
-256 x 128 launch for the last columns of down_proj), the Qwen3-14B gate_proj with int8 moments,
-and the 8-rule sweep at T = 16384 with bf16 and fp8 inputs.
+covered: the Llama-3.1-8B down_proj at T = 4096 (768 256 x 256 wide tiles and 256 128 x 256
+half-wide tiles in one launch), the wide tiles at T = 8192 (alone for q_proj, with half-wide
+tiles on the last row blocks of gate_proj and the last columns of down_proj), the Qwen3-14B
+gate_proj with int8 moments on 256 x 128 and 128 x 128 tiles, and the 8-rule sweep at
+T = 16384 with bf16 and fp8 inputs.
 
 Exact-sum inputs (synth.integer_case: inputs on a dyadic grid, every fp32 partial sum of the
 gradient is exact in any order for T <= 65536) make the kernel's gradient equal to the oracle's
@@ -78,7 +79,7 @@ def _step_exact(lib, X, dY, g, W, m, v, opt, h, t, seed, w_fmt, state_fmt, tag):
 
 
 def test_exact_down_proj_headline_launch(lib):
-    """W[4096, 14336], T = 4096: the benchmark's launch (full and half tiles), AdamW, 2 steps."""
+    """W[4096, 14336], T = 4096: the benchmark's launch (wide and half-wide tiles), AdamW, 2 steps."""
     w = synth.WORKLOADS[2]
     L = w.layers[0]
     X, dY = synth.integer_case(2001, w.T, L.N, L.K, "bf16")
@@ -93,9 +94,9 @@ def test_exact_down_proj_headline_launch(lib):
 
 @pytest.mark.parametrize("li", [0, 4, 6], ids=["q_proj", "gate_proj", "down_proj"])
 def test_exact_wide_tiles_T8192_with_dgrad(lib, li):
-    """T = 8192: q_proj runs on 256 x 256 tiles only; gate_proj on 48 wide row blocks plus a
-    256 x 128 launch (as half tiles) for its last 8 row blocks; down_proj on 48 wide column
-    blocks plus a 256 x 128 launch for the last 16 columns of 128.  dgrad first, on the old
+    """T = 8192: q_proj runs on 256 x 256 tiles only; gate_proj on 48 wide row blocks and its
+    last 8 row blocks as 128 x 256 half-wide tiles, down_proj on 48 wide column blocks and its
+    last 8 256-column blocks as half-wide tiles, each in one launch.  dgrad first, on the old
     weight."""
     w = synth.WORKLOADS[3]
     L = w.layers[li]

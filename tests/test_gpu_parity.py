@@ -469,7 +469,7 @@ FULL_RULES = [(opt, s) for opt in synth.OPTIMIZERS for s in ("f32", "int8")]
 
 @pytest.mark.parametrize("opt,state_fmt", FULL_RULES, ids=["-".join(c) for c in FULL_RULES])
 def test_v2_full_tiles_every_rule_exact_oracle_fed(lib, opt, state_fmt):
-    """Every rule and moment format on the benchmark's 256 x 128 tiles (with their two-half
+    """Every rule and moment format on the 256 x 128 tiles (with their two-half
     epilogue) and half tiles in one launch, exact-sum inputs, steps 1 and 6 from the oracle's
     stored state."""
     rng = np.random.default_rng(43)

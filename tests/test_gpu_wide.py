@@ -1,16 +1,21 @@
 """GPU tests of the wide-tile path of the fused step: 256 x 256 tiles, one 8-wave workgroup per CU.
 
-bf16 inputs with T >= 8192 take wide tiles where they fill whole rounds of one workgroup per CU;
-the remaining columns run on the 256 x 128 path in a second launch.  Every element's token sum
-runs in the same order on both paths, so the fused step must equal the unfused path (the
-256 x 128 GEMM to HBM, then the optimizer kernel) bitwise, whatever mix of launches covers the
-weight.  Shapes (on 256 CUs): 4096 x 4096 is 256 wide tiles (one launch); 2048 x 8192 is 8 x 32
-wide tiles; 4096 x 4224 adds one 128-column block, run as 32 half tiles in the second launch;
-6144 x 4096 has no whole-round column split (24 row blocks), so its first 16 row blocks run as
-256 wide tiles and the last 8 on the 256 x 128 path (as 512 half tiles for bf16 inputs).
-T = 8193 and 8200 leave a ragged last slab of tokens.  fp8 inputs follow the same rule.  The
-full-size workload tests (the Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384 in
-bf16 and fp8) check this path against the fp64 oracle on sampled rows.
+bf16 inputs with T >= 8192 take wide tiles where K is a multiple of 256: whole rounds of wide
+tiles, and where the R wide tiles leave a remainder r over the CUs, the last r / (N / 256)
+256-column blocks (or the last r / (K / 256) row blocks) as 2 r half-wide tiles of 128 x 256
+in the same launch, half of them dispatched first.  Otherwise whole rounds of wide tiles cover
+part of the weight and the rest runs on the 256 x 128 path in a second launch.  Every
+element's token sum runs in the same order on all these tiles, so the fused step must equal
+the unfused path (the 256 x 128 GEMM to HBM, then the optimizer kernel) bitwise, whatever mix
+of tiles and launches covers the weight.  Shapes (on 256 CUs): 4096 x 4096 is 256 wide tiles;
+2048 x 8192 is 8 x 32 wide tiles; 4096 x 4224 (K / 256 not whole) takes 256 wide tiles and
+runs its last 128-column block as 32 half tiles in the second launch; 6144 x 4096 is 384 wide
+tiles, so its last 8 row blocks run as 256 half-wide tiles; 4096 x 5120 (320 tiles) and
+2048 x 9216 (288) run their last 4 256-column blocks as 128 and 64 half-wide tiles.  T = 8193
+and 8200 leave a ragged last slab of tokens.  fp8 inputs have no half-wide tiles: whole
+rounds of wide tiles, the rest on the 256 x 128 path.  The full-size workload tests (the
+Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384 in bf16 and fp8) check this
+path against the fp64 oracle on sampled rows.
 """
 from __future__ import annotations
 
@@ -47,7 +52,8 @@ CASES = [((4096, 4096), "adamw", "bf16", "f32", 8192), ((4096, 4224), "adamw", "
          ((4096, 4224), "radam", "bf16", "int8", 8192), ((2048, 8192), "rmsprop", "bf16", "f32", 8192),
          ((4096, 4096), "adagrad", "bf16", "f32", 8193), ((4096, 4224), "sgd", "f32", "f32", 8192),
          ((2048, 8192), "sgd_momentum", "bf16", "int8", 8192), ((6144, 4096), "adamw", "bf16", "f32", 8192),
-         ((6144, 4096), "lion", "bf16", "int8", 8200), ((6144, 4096), "adamw", "bf16", "int8dyn", 8192)]
+         ((6144, 4096), "lion", "bf16", "int8", 8200), ((6144, 4096), "adamw", "bf16", "int8dyn", 8192),
+         ((4096, 5120), "nadam", "bf16", "int8", 8193), ((2048, 9216), "adamw", "bf16", "f32", 8192)]
 
 
 @pytest.mark.parametrize("shape,opt,w_fmt,state_fmt,Tn", CASES,
@@ -98,7 +104,7 @@ def test_wide_fp8_fused_equals_unfused_bitwise(lib, shape, opt, w_fmt, state_fmt
 
 
 def test_wide_llama_down_proj_equals_unfused(lib):
-    """Llama-3.1-8B down_proj at T = 8192: 768 wide tiles, then 256 tiles of 256 x 128."""
+    """Llama-3.1-8B down_proj at T = 8192: 768 wide tiles and 256 half-wide tiles, one launch."""
     Nn, Kn, Tn = 4096, 14336, 8192
     _say("wide fused vs unfused, down_proj T=8192")
     g = torch.Generator(device="cuda").manual_seed(11)
