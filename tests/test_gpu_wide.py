@@ -12,8 +12,9 @@ of tiles and launches covers the weight.  Shapes (on 256 CUs): 4096 x 4096 is 25
 runs its last 128-column block as 32 half tiles in the second launch; 6144 x 4096 is 384 wide
 tiles, so its last 8 row blocks run as 256 half-wide tiles; 4096 x 5120 (320 tiles) and
 2048 x 9216 (288) run their last 4 256-column blocks as 128 and 64 half-wide tiles.  T = 8193
-and 8200 leave a ragged last slab of tokens.  fp8 inputs have no half-wide tiles: whole
-rounds of wide tiles, the rest on the 256 x 128 path.  The full-size workload tests (the
+and 8200 leave a ragged last slab of tokens.  The half-wide plan starts at T = 4096, so
+4096 x 5120 and 2048 x 9216 also run at T = 4096 and 4100.  fp8 inputs have no half-wide
+tiles: whole rounds of wide tiles, the rest on the 256 x 128 path.  The full-size workload tests (the
 Llama-3.1-8B block at T = 8192, the optimizer sweep at T = 16384 in bf16 and fp8) check this
 path against the fp64 oracle on sampled rows.
 """
@@ -53,7 +54,8 @@ CASES = [((4096, 4096), "adamw", "bf16", "f32", 8192), ((4096, 4224), "adamw", "
          ((4096, 4096), "adagrad", "bf16", "f32", 8193), ((4096, 4224), "sgd", "f32", "f32", 8192),
          ((2048, 8192), "sgd_momentum", "bf16", "int8", 8192), ((6144, 4096), "adamw", "bf16", "f32", 8192),
          ((6144, 4096), "lion", "bf16", "int8", 8200), ((6144, 4096), "adamw", "bf16", "int8dyn", 8192),
-         ((4096, 5120), "nadam", "bf16", "int8", 8193), ((2048, 9216), "adamw", "bf16", "f32", 8192)]
+         ((4096, 5120), "nadam", "bf16", "int8", 8193), ((2048, 9216), "adamw", "bf16", "f32", 8192),
+         ((4096, 5120), "adamw", "bf16", "int8", 4096), ((2048, 9216), "lion", "f32", "f32", 4100)]
 
 
 @pytest.mark.parametrize("shape,opt,w_fmt,state_fmt,Tn", CASES,
