@@ -193,9 +193,9 @@ forge_status forge_linear_backward_step(const forge_tensor* X, const forge_tenso
  * tile; a step tile contracts dY and X, then, before it writes W, waits until every dX tile of
  * its 128 columns has finished reading them.  dX comes out bitwise as from forge_dgrad.  W, m
  * and v come out bitwise as from forge_linear_backward_step wherever that call's step runs on
- * the 256 x 128 or 256 x 256 tiles (N % 256 == 0 and at least 128 tiles of 256 x 128); on
- * smaller layers it uses 128 x 128 tiles with their own token order, and the two agree within
- * the fp32 summation bound of the gradient.
+ * the 256 x 128, 256 x 256 or 128 x 256 tiles (N % 256 == 0 and at least 128 tiles of
+ * 256 x 128); on smaller layers it uses 128 x 128 tiles with their own token order, and the two
+ * agree within the fp32 summation bound of the gradient.
  *
  * Arguments as forge_linear_backward_step (BF16 X, dY, W and dX), and N % 256 == 0, K % 128 == 0
  * (else FORGE_ERR_SHAPE).  workspace: device memory of at least

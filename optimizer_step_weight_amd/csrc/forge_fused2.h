@@ -1,6 +1,7 @@
 // forge_fused2.h -- the fused step for bf16 inputs on the LDS-DMA path (forge_mainloop2.h):
 // 256 x 128 tiles, two workgroups per CU, with 128 x 128 half tiles balancing the last round of
-// a launch, and 256 x 256 tiles in one 8-wave workgroup per CU for long token counts.
+// a launch, and 256 x 256 tiles in one 8-wave workgroup per CU, with 128 x 256 half-wide tiles
+// balancing theirs (the launch plans are in forge_plan.h).
 // FORGE explainer (gist.science), Technical Summary section 2 "Core Mechanism".
 //
 // Instantiated per moment format in forge_fused2_f32.hip, forge_fused2_q8.hip (linear 8-bit
