@@ -4,8 +4,8 @@ The library is called as the benchmark calls it, so every tile path of the timed
 covered: the Llama-3.1-8B down_proj at T = 4096 (768 256 x 256 wide tiles and 256 128 x 256
 half-wide tiles in one launch), the wide tiles at T = 8192 (alone for q_proj, with half-wide
 tiles on the last row blocks of gate_proj and the last columns of down_proj), the Qwen3-14B
-gate_proj with int8 moments on 256 x 128 and 128 x 128 tiles, and the 8-rule sweep at
-T = 16384 with bf16 and fp8 inputs.
+gate_proj with int8 moments (wide tiles, its last 4 row blocks as half-wide tiles), and the
+8-rule sweep at T = 16384 with bf16 and fp8 inputs.
 
 Exact-sum inputs (synth.integer_case: inputs on a dyadic grid, every fp32 partial sum of the
 gradient is exact in any order for T <= 65536) make the kernel's gradient equal to the oracle's
